@@ -1,0 +1,195 @@
+"""Checks that tie the FP64 oracle to the pages and to mathematics.
+
+Each ``pin_*`` function takes a decode function with the signature of
+``oracle.mla_decode_ref`` (BF16 bit inputs) or ``oracle.mla_decode_ref_f64``
+and raises AssertionError when it disagrees with a fact fixed outside the
+oracle. They are collected as tests in ``test_oracle_pins.py`` and reused by
+``test_oracle_mutations.py``, which plants mistakes in the oracle and checks
+that some pin catches each one.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+from workloads import make_inputs, permute_pages, bf16_bits_to_f32
+
+PAGE = 64
+
+
+def _f64(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _paged(rows: np.ndarray, seed: int, extra_pages: int = 2):
+    """Place logical rows [N, 576] (float64) into shuffled pages; returns
+    kv [NB, 64, 1, 576], block_table [1, nb]. Unused slots hold NaN so any
+    read past N shows up."""
+    n = rows.shape[0]
+    nb = (n + PAGE - 1) // PAGE
+    total = nb + extra_pages
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(total)[:nb]
+    kv = np.full((total, PAGE, 1, rows.shape[1]), np.nan)
+    for t in range(n):
+        kv[perm[t // PAGE], t % PAGE, 0] = rows[t]
+    return kv, perm[None, :].astype(np.int32)
+
+
+# (a) Non-absorbed identity: the MLA page's up-projected form equals the
+# absorbed form used by decode (q_abs = [W_UK q_nope ; q_rope], o = o_lat W_UV).
+def pin_nonabsorbed_identity(ref_f64, seed=11, n=150, heads=4, dn=128, dv=96):
+    rng = np.random.default_rng(seed)
+    c_kv = rng.standard_normal((n, 512))
+    k_rope = rng.standard_normal((n, 64))
+    w_uk = rng.standard_normal((heads, 512, dn)) / math.sqrt(512)
+    w_uv = rng.standard_normal((heads, 512, dv)) / math.sqrt(512)
+    q_nope = rng.standard_normal((heads, dn))
+    q_rope = rng.standard_normal((heads, 64))
+    scale = 1.0 / math.sqrt(576)
+    o_ref, lse_ref = oracle.mla_nonabsorbed_ref(c_kv, k_rope, q_nope, q_rope, w_uk, w_uv, scale)
+
+    q_abs = np.concatenate([np.einsum("hcd,hd->hc", w_uk, q_nope), q_rope], axis=1)
+    kv, table = _paged(np.concatenate([c_kv, k_rope], axis=1), seed)
+    out, lse = ref_f64(q_abs[None, None], kv, table, np.array([n]), scale, False)
+    o_abs = np.einsum("hc,hcv->hv", out[0, 0], w_uv)
+    rel = np.abs(o_abs - o_ref).max() / np.abs(o_ref).max()
+    assert rel < 1e-12, f"absorbed vs non-absorbed output rel err {rel}"
+    assert np.abs(lse[0, 0] - lse_ref).max() < 1e-12, "absorbed vs non-absorbed lse"
+
+
+# (b) Page placement does not matter: moving physical pages and rewriting the
+# block table leaves the logical sequences, hence the result, unchanged.
+def pin_page_permutation(ref, seed=12):
+    inp = make_inputs([37, 100, 64, 129], s_q=2, h_q=16, seed=seed, causal=True, extra_blocks=1)
+    out0, lse0 = ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale, True)
+    moved = permute_pages(inp, seed + 1)
+    out1, lse1 = ref(moved.q_bits, moved.kv_bits, moved.block_table, moved.seqlens, moved.scale, True)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1), "page permutation changed result"
+
+
+# (c) One cached token: softmax weight 1, so out = V_0 and lse = scale <q, K_0>.
+def pin_single_token(ref, seed=13):
+    inp = make_inputs([1, 1, 1], s_q=1, h_q=16, seed=seed)
+    out, lse = ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale, False)
+    for b in range(3):
+        k0 = _f64(inp.kv_bits[inp.block_table[b, 0], 0, 0])
+        q = _f64(inp.q_bits[b, 0])
+        assert np.array_equal(out[b, 0], np.broadcast_to(k0[:512], (16, 512))), "out != V_0"
+        s = float(np.float32(inp.scale)) * np.array([math.fsum(q[h] * k0) for h in range(16)])
+        assert np.abs(lse[b, 0] - s).max() < 1e-12, "lse != scale <q,K_0>"
+
+
+# (d) Equal scores: with q's latent part zero and one shared rotary key, all
+# scores equal c, so out = mean of V and lse = c + ln N. With q = 0, lse = ln N.
+def pin_equal_scores(ref_f64, seed=14, n=150):
+    rng = np.random.default_rng(seed)
+    latent = rng.standard_normal((n, 512))
+    rope = rng.standard_normal(64)
+    rows = np.concatenate([latent, np.broadcast_to(rope, (n, 64))], axis=1)
+    kv, table = _paged(rows, seed)
+    q = np.zeros((1, 1, 3, 576))
+    q[0, 0, 1, 512:] = rng.standard_normal(64)
+    q[0, 0, 2, 512:] = rng.standard_normal(64)
+    scale = 1.0 / 24.0
+    out, lse = ref_f64(q, kv, table, np.array([n]), scale, False)
+    mean_v = latent.mean(axis=0)
+    for h in range(3):
+        c = scale * math.fsum(q[0, 0, h, 512:] * rope)
+        assert abs(lse[0, 0, h] - (c + math.log(n))) < 1e-12, "lse != c + ln N"
+        assert np.abs(out[0, 0, h] - mean_v).max() < 1e-12, "out != mean V"
+
+
+# (e) Causal reductions: with s_q = 2 under the causal mask, token 1 equals a
+# single-token decode over all N keys and token 0 one over the first N-1;
+# with s_q = 1 the causal mask changes nothing.
+def pin_causal_reductions(ref, seed=15):
+    inp = make_inputs([1, 2, 64, 65, 130], s_q=2, h_q=16, seed=seed, causal=True)
+    out, lse = ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale, True)
+    for i in (0, 1):
+        lens = np.maximum(inp.seqlens - (1 - i), 0).astype(np.int32)
+        o1, l1 = ref(inp.q_bits[:, i:i + 1], inp.kv_bits, inp.block_table, lens, inp.scale, False)
+        assert np.array_equal(out[:, i], o1[:, 0]), f"causal token {i} output"
+        assert np.array_equal(lse[:, i], l1[:, 0]), f"causal token {i} lse"
+    # the sequence of length 1 has no visible key for token 0
+    assert np.all(np.isneginf(lse[0, 0])) and not np.any(out[0, 0]), "empty causal row"
+    single = make_inputs([5, 70], s_q=1, h_q=16, seed=seed + 1)
+    a = ref(single.q_bits, single.kv_bits, single.block_table, single.seqlens, single.scale, True)
+    b = ref(single.q_bits, single.kv_bits, single.block_table, single.seqlens, single.scale, False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "causal s_q=1 not a no-op"
+
+
+# (f) Combine identity: attending over random disjoint key chunks and merging
+# with the log-sum-exp rule reproduces attention over all keys.
+def pin_combine_identity(attend, combine, seed=16, n=300, rows=8):
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((n, 576))
+    q = rng.standard_normal((rows, 576))
+    scale = 1.0 / 24.0
+    o_full, l_full = attend(q, k, [n] * rows, scale)
+    cuts = np.sort(rng.choice(np.arange(1, n), size=5, replace=False))
+    bounds = [0, *cuts.tolist(), n]
+    parts_o, parts_l = [], []
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        o, l = attend(q, k[lo:hi], [hi - lo] * rows, scale)
+        parts_o.append(o)
+        parts_l.append(l)
+    # an empty chunk carries no weight
+    parts_o.append(np.zeros((rows, 512)))
+    parts_l.append(np.full(rows, -np.inf))
+    o, l = combine(np.stack(parts_o), np.stack(parts_l))
+    assert np.abs(o - o_full).max() < 1e-13 and np.abs(l - l_full).max() < 1e-13, "combine"
+    o_e, l_e = combine(np.zeros((2, 3, 512)), np.full((2, 3), -np.inf))
+    assert not np.any(o_e) and np.all(np.isneginf(l_e)), "combine of empty parts"
+
+
+# (i) Brute force: pure-Python loops with exactly rounded sums on tiny inputs.
+def pin_bruteforce(ref_f64, seed=17):
+    for causal in (False, True):
+        inp = make_inputs([3, 70, 1], s_q=2, h_q=2, seed=seed + causal, causal=causal)
+        q, kv = _f64(inp.q_bits), _f64(inp.kv_bits)
+        o_bf, l_bf = oracle.mla_decode_bruteforce(q, kv, inp.block_table, inp.seqlens,
+                                                  float(np.float32(inp.scale)), causal)
+        o, l = ref_f64(q, kv, inp.block_table, inp.seqlens, float(np.float32(inp.scale)), causal)
+        assert np.abs(o - o_bf).max() < 1e-12, "output vs brute force"
+        fin = np.isfinite(l_bf)
+        assert np.array_equal(fin, np.isfinite(l)), "empty rows vs brute force"
+        assert np.abs(l[fin] - l_bf[fin]).max() < 1e-12, "lse vs brute force"
+
+
+# (j) Bounds: max_t s_t <= lse <= max_t s_t + ln L, and every output is a
+# convex combination of value rows (inside their per-column range).
+def pin_bounds(ref, seed=18):
+    inp = make_inputs([40, 200], s_q=1, h_q=16, seed=seed)
+    out, lse = ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale, False)
+    for b, n in enumerate(inp.seqlens):
+        rows = np.stack([_f64(inp.kv_bits[inp.block_table[b, t // PAGE], t % PAGE, 0]) for t in range(n)])
+        q = _f64(inp.q_bits[b, 0])
+        s = float(np.float32(inp.scale)) * (q @ rows.T)
+        smax = s.max(axis=1)
+        assert np.all(lse[b, 0] >= smax - 1e-12) and np.all(lse[b, 0] <= smax + math.log(n) + 1e-12), "lse bounds"
+        lo, hi = rows[:, :512].min(axis=0), rows[:, :512].max(axis=0)
+        assert np.all(out[b, 0] >= lo - 1e-12) and np.all(out[b, 0] <= hi + 1e-12), "convexity"
+
+
+# (k) Two keys, worked by hand: with scores s0, s1 the weights are the
+# logistic function of their difference.
+def pin_two_keys(ref_f64):
+    rows = np.zeros((2, 576))
+    rows[0, 0], rows[1, 0] = 1.0, -1.0        # V_0 = e_0, V_1 = -e_0
+    rows[0, 1], rows[1, 1] = 2.0, 5.0         # second latent coordinate
+    rows[:, 512] = [3.0, 1.0]                 # rotary coordinate
+    q = np.zeros((1, 1, 1, 576))
+    q[0, 0, 0, 512] = 1.0                     # s_t = scale * rope_t
+    kv, table = _paged(rows, 3)
+    scale = 0.5
+    out, lse = ref_f64(q, kv, table, np.array([2]), scale, False)
+    s0, s1 = 1.5, 0.5
+    w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert abs(lse[0, 0, 0] - (s0 + math.log1p(math.exp(s1 - s0)))) < 1e-15
+    assert abs(out[0, 0, 0, 0] - (2 * w0 - 1)) < 1e-15
+    assert abs(out[0, 0, 0, 1] - (2 * w0 + 5 * (1 - w0))) < 1e-14
+    assert not np.any(out[0, 0, 0, 2:])

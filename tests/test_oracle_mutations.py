@@ -1,0 +1,133 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one of them. A pin suite that still passes with a dropped term, a
+wrong index or sign, or a transposed operand would not be pinning anything.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.mla_ref as R
+import oracle_pins as P
+
+
+def _run_all_pins():
+    """Returns the names of pins that fail (AssertionError or any exception)."""
+    pins = [
+        ("nonabsorbed", lambda: P.pin_nonabsorbed_identity(R.mla_decode_ref_f64)),
+        ("permutation", lambda: P.pin_page_permutation(R.mla_decode_ref)),
+        ("single_token", lambda: P.pin_single_token(R.mla_decode_ref)),
+        ("equal_scores", lambda: P.pin_equal_scores(R.mla_decode_ref_f64)),
+        ("causal", lambda: P.pin_causal_reductions(R.mla_decode_ref)),
+        ("combine", lambda: P.pin_combine_identity(R.attend_rows, R.lse_combine_ref)),
+        ("bruteforce", lambda: P.pin_bruteforce(R.mla_decode_ref_f64)),
+        ("bounds", lambda: P.pin_bounds(R.mla_decode_ref)),
+        ("two_keys", lambda: P.pin_two_keys(R.mla_decode_ref_f64)),
+    ]
+    failed = []
+    with np.errstate(all="ignore"):
+        for name, fn in pins:
+            try:
+                fn()
+            except Exception:  # noqa: BLE001 - any failure counts as caught
+                failed.append(name)
+    return failed
+
+
+def _attend_variant(scores_fn=None, values_fn=None, lse_fn=None, weight_fn=None):
+    """attend_rows with one step replaced."""
+    def attend(q, k, lengths, scale):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        out = np.zeros((q.shape[0], 512))
+        lse = np.full(q.shape[0], -np.inf)
+        if k.shape[0] == 0:
+            return out, lse
+        scores = scores_fn(q, k, scale) if scores_fn else scale * (q @ k.T)
+        values = values_fn(k) if values_fn else k[:, :512]
+        for r in range(q.shape[0]):
+            L = int(lengths[r])
+            if L == 0:
+                continue
+            s = scores[r, :L]
+            m = s.max()
+            total = np.exp(s - m).sum()
+            lse[r] = lse_fn(m, total) if lse_fn else m + math.log(total)
+            p = weight_fn(s, m, lse[r]) if weight_fn else np.exp(s - lse[r])
+            out[r] = p @ values[:L]
+        return out, lse
+    return attend
+
+
+def _gather_variant(page_of, slot_of):
+    def gather(kv, table_row, n):
+        if n == 0:
+            return np.zeros((0, kv.shape[-1]), dtype=kv.dtype)
+        t = np.arange(n)
+        return kv[np.asarray(table_row)[page_of(t)], slot_of(t), 0, :]
+    return gather
+
+
+MUTATIONS = {
+    "gather_page_slot_swapped": ("gather_sequence_rows",
+                                 _gather_variant(lambda t: t % 64, lambda t: t // 64)),
+    "gather_slot_off_by_one": ("gather_sequence_rows",
+                               _gather_variant(lambda t: t // 64, lambda t: (t + 1) % 64)),
+    "gather_ignores_block_table": ("gather_sequence_rows",
+                                   _gather_variant(lambda t: t // 64 * 0, lambda t: t % 64)),
+    "rotary_term_dropped": ("attend_rows", _attend_variant(
+        scores_fn=lambda q, k, sc: sc * (q[:, :512] @ k[:, :512].T))),
+    "scale_missing": ("attend_rows", _attend_variant(scores_fn=lambda q, k, sc: q @ k.T)),
+    "scale_squared": ("attend_rows", _attend_variant(scores_fn=lambda q, k, sc: sc * sc * (q @ k.T))),
+    "values_take_rotary_part": ("attend_rows", _attend_variant(values_fn=lambda k: k[:, 64:])),
+    "lse_sign": ("attend_rows", _attend_variant(lse_fn=lambda m, tot: m - math.log(tot))),
+    "lse_log2": ("attend_rows", _attend_variant(lse_fn=lambda m, tot: m + math.log2(tot))),
+    "weights_not_normalised": ("attend_rows", _attend_variant(weight_fn=lambda s, m, l: np.exp(s - m))),
+    "causal_off_by_one": ("visible_length",
+                          lambda n, s_q, i, c: n if not c else max(0, min(n, n - s_q + i))),
+    "causal_reversed": ("visible_length",
+                        lambda n, s_q, i, c: n if not c else max(0, min(n, n - i))),
+    "causal_ignored": ("visible_length", lambda n, s_q, i, c: n),
+}
+
+
+def _combine_plain_average(o_parts, lse_parts):
+    o_parts = np.asarray(o_parts)
+    lse_parts = np.asarray(lse_parts)
+    fin = np.isfinite(lse_parts)
+    cnt = np.maximum(fin.sum(axis=0), 1)
+    m = np.where(fin, lse_parts, -np.inf).max(axis=0)
+    lse = m + np.log(np.where(fin, np.exp(lse_parts - np.where(np.isfinite(m), m, 0)), 0).sum(axis=0))
+    return (o_parts * fin[..., None]).sum(axis=0) / cnt[..., None], lse
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _run_all_pins() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(R, attr, fn)
+    failed = _run_all_pins()
+    assert failed, f"mutation {name} passed every pin"
+
+
+def test_layout_mutation_token_head_order_is_caught(monkeypatch):
+    """Rows of a sequence flattened as (head, token) instead of (token, head)."""
+    real = R.mla_decode_ref_f64
+
+    def swapped(q, kv, table, seqlens, scale, causal, seqs=None):
+        q = np.asarray(q, dtype=np.float64)
+        qs = np.ascontiguousarray(q.transpose(0, 2, 1, 3)).reshape(q.shape)
+        return real(qs, kv, table, seqlens, scale, causal, seqs)
+
+    monkeypatch.setattr(R, "mla_decode_ref_f64", swapped)
+    assert _run_all_pins(), "token/head order swap passed every pin"
+
+
+def test_combine_mutation_is_caught(monkeypatch):
+    monkeypatch.setattr(R, "lse_combine_ref", _combine_plain_average)
+    assert "combine" in _run_all_pins()

@@ -1,0 +1,40 @@
+"""The FP64 oracle against facts fixed outside it (CPU only)."""
+
+import oracle
+import oracle_pins as P
+
+
+def test_nonabsorbed_identity():
+    P.pin_nonabsorbed_identity(oracle.mla_decode_ref_f64)
+
+
+def test_page_permutation_invariance():
+    P.pin_page_permutation(oracle.mla_decode_ref)
+
+
+def test_single_token():
+    P.pin_single_token(oracle.mla_decode_ref)
+
+
+def test_equal_scores():
+    P.pin_equal_scores(oracle.mla_decode_ref_f64)
+
+
+def test_causal_reductions():
+    P.pin_causal_reductions(oracle.mla_decode_ref)
+
+
+def test_combine_identity():
+    P.pin_combine_identity(oracle.attend_rows, oracle.lse_combine_ref)
+
+
+def test_bruteforce():
+    P.pin_bruteforce(oracle.mla_decode_ref_f64)
+
+
+def test_bounds():
+    P.pin_bounds(oracle.mla_decode_ref)
+
+
+def test_two_keys_by_hand():
+    P.pin_two_keys(oracle.mla_decode_ref_f64)

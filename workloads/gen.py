@@ -1,0 +1,210 @@
+"""Seeded generator for paged MLA decode inputs.
+
+Inputs follow the problem statement of the FlashMLA overview page (BF16 query
+and cache, a paged cache with 64-token blocks, variable-length sequences) and
+the cache-row shape used throughout: 576 values per token, the first 512 being
+the compressed latent c_KV and the last 64 the rotary part.
+
+Recipe (fixed so every size and total is reproducible):
+
+1. ``rng = numpy.random.default_rng(seed)``.
+2. Sequence lengths are drawn first when the workload asks for random ones.
+3. ``NB = sum(ceil(N_b / 64))`` physical pages; ``perm = rng.permutation(NB)``;
+   sequence ``b`` takes the next ``ceil(N_b / 64)`` entries of ``perm`` in
+   order. The block-table row width is ``max_b ceil(N_b / 64)`` and unused
+   entries hold -1.
+4. ``q = rng.standard_normal((B, S_q, H_q, 576), float32)`` and
+   ``kv = rng.standard_normal((NB, 64, 1, 576), float32)``, both rounded to
+   BF16 with round-to-nearest-even on the bit pattern.
+5. ``scale = 1/sqrt(576)`` as float32.
+
+Everything here is input preparation only.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+HEAD_DIM = 576      # latent (512) + rotary part (64) per cache row
+HEAD_DIM_V = 512    # value width: the latent part of the same row
+PAGE_SIZE = 64      # tokens per physical page
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """A named synthetic decode workload."""
+
+    name: str
+    seed: int
+    batch: int
+    s_q: int
+    h_q: int
+    causal: bool
+    seqlens_fixed: Optional[tuple] = None       # explicit lengths, or
+    seqlens_uniform: Optional[tuple] = None     # (lo, hi) inclusive, drawn
+    description: str = ""
+
+    def draw_seqlens(self, rng: np.random.Generator) -> np.ndarray:
+        if self.seqlens_fixed is not None:
+            return np.asarray(self.seqlens_fixed, dtype=np.int32)
+        lo, hi = self.seqlens_uniform
+        return rng.integers(lo, hi, size=self.batch, endpoint=True).astype(np.int32)
+
+
+WORKLOADS = {
+    "tiny": Workload(
+        "tiny", 1, 2, 1, 16, False, seqlens_fixed=(37, 100),
+        description="batch 2, seqlens {37,100}, s_q=1, h_q=16"),
+    "memory_bound": Workload(
+        "memory_bound", 2, 64, 1, 16, False, seqlens_uniform=(3072, 5120),
+        description="batch 64, seqlens U[3072,5120], s_q=1, h_q=16"),
+    "compute_leaning": Workload(
+        "compute_leaning", 3, 128, 1, 128, False, seqlens_fixed=(4096,) * 128,
+        description="batch 128, seqlen 4096, s_q=1, h_q=128"),
+    "long_context": Workload(
+        "long_context", 4, 4, 1, 64, False, seqlens_fixed=(1024, 16384, 32768, 65536),
+        description="batch 4, seqlens {1K,16K,32K,64K}, s_q=1, h_q=64"),
+    "multi_token": Workload(
+        "multi_token", 5, 132, 2, 128, True, seqlens_uniform=(1, 8192),
+        description="batch 132, seqlens U[1,8192], s_q=2 causal, h_q=128"),
+}
+
+
+@dataclasses.dataclass
+class MlaInputs:
+    """Host-side inputs. BF16 tensors are held as their uint16 bit patterns."""
+
+    seqlens: np.ndarray        # int32 [B]
+    block_table: np.ndarray    # int32 [B, max_blocks]
+    q_bits: np.ndarray         # uint16 [B, S_q, H_q, 576]
+    kv_bits: np.ndarray        # uint16 [NB, 64, 1, 576]
+    scale: float               # exactly representable in float32
+    causal: bool
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def s_q(self) -> int:
+        return int(self.q_bits.shape[1])
+
+    @property
+    def h_q(self) -> int:
+        return int(self.q_bits.shape[2])
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv_bits.shape[0])
+
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> BF16 bit pattern (uint16), round to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = np.uint16(0x7FC0)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """BF16 bit pattern -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _standard_normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 25) -> np.ndarray:
+    """Draw N(0,1) float32 in one stream and round to BF16 bits, chunk by chunk
+    (same values as one big draw, bounded temporary memory)."""
+    total = int(np.prod(shape))
+    out = np.empty(total, dtype=np.uint16)
+    done = 0
+    while done < total:
+        n = min(chunk, total - done)
+        out[done:done + n] = bf16_round_bits(rng.standard_normal(n, dtype=np.float32))
+        done += n
+    return out.reshape(shape)
+
+
+def make_inputs(seqlens: Sequence[int], s_q: int, h_q: int, seed: int,
+                causal: bool = False, rng: Optional[np.random.Generator] = None,
+                extra_blocks: int = 0) -> MlaInputs:
+    """Build inputs for explicit sequence lengths.
+
+    ``rng`` lets a workload draw its lengths from the same stream first.
+    ``extra_blocks`` widens the block table beyond the longest sequence (the
+    extra entries are padding, -1).
+    """
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    if seqlens.ndim != 1 or seqlens.size == 0 or (seqlens < 0).any():
+        raise ValueError("seqlens must be a non-empty 1-D array of non-negative ints")
+    pages = (seqlens.astype(np.int64) + PAGE_SIZE - 1) // PAGE_SIZE
+    nb = int(pages.sum())
+    perm = rng.permutation(nb).astype(np.int32) if nb > 0 else np.zeros(0, np.int32)
+    width = max(int(pages.max()), 1) + int(extra_blocks)
+    table = np.full((seqlens.size, width), -1, dtype=np.int32)
+    cur = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[cur:cur + n]
+        cur += int(n)
+    q_bits = _standard_normal_bf16(rng, (seqlens.size, s_q, h_q, HEAD_DIM))
+    kv_bits = _standard_normal_bf16(rng, (max(nb, 1), PAGE_SIZE, 1, HEAD_DIM))
+    scale = float(np.float32(1.0 / math.sqrt(HEAD_DIM)))
+    return MlaInputs(seqlens, table, q_bits, kv_bits, scale, bool(causal))
+
+
+def make_workload_inputs(name: str) -> MlaInputs:
+    """Inputs of a named workload, with its own seed."""
+    w = WORKLOADS[name]
+    rng = np.random.default_rng(w.seed)
+    seqlens = w.draw_seqlens(rng)
+    return make_inputs(seqlens, w.s_q, w.h_q, w.seed, w.causal, rng=rng)
+
+
+def permute_pages(inp: MlaInputs, seed: int) -> MlaInputs:
+    """Move every physical page to a new slot and rewrite the block table to
+    match. The logical content of every sequence is unchanged."""
+    rng = np.random.default_rng(seed)
+    nb = inp.num_pages
+    pi = rng.permutation(nb).astype(np.int32)
+    kv = np.empty_like(inp.kv_bits)
+    kv[pi] = inp.kv_bits
+    table = inp.block_table.copy()
+    valid = table >= 0
+    valid &= table < nb
+    table[valid] = pi[table[valid]]
+    return dataclasses.replace(inp, block_table=table, kv_bits=kv)
+
+
+def poison_page_tails(inp: MlaInputs, bits: int = 0x7FC0) -> MlaInputs:
+    """Fill the unused rows of every partially filled last page with ``bits``
+    (a BF16 NaN by default)."""
+    kv = inp.kv_bits.copy()
+    for b, n in enumerate(inp.seqlens):
+        n = int(n)
+        if n % PAGE_SIZE == 0:
+            continue
+        phys = int(inp.block_table[b, n // PAGE_SIZE])
+        kv[phys, n % PAGE_SIZE:] = np.uint16(bits)
+    return dataclasses.replace(inp, kv_bits=kv)
+
+
+def poison_block_table_padding(inp: MlaInputs) -> MlaInputs:
+    """Fill block-table entries past each sequence's last page with -1 and
+    INT32_MAX, alternating."""
+    table = inp.block_table.copy()
+    for b, n in enumerate(inp.seqlens):
+        used = (int(n) + PAGE_SIZE - 1) // PAGE_SIZE
+        pad = table.shape[1] - used
+        if pad > 0:
+            vals = np.where(np.arange(pad) % 2 == 0, -1, np.iinfo(np.int32).max)
+            table[b, used:] = vals.astype(np.int32)
+    return dataclasses.replace(inp, block_table=table)
