@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of paged MLA decode on one MI355X.
+
+One step = the whole hot path on one batch: the split metadata, the decode
+kernel and the combine kernel (mla_get_split_metadata + mla_decode_fwd).
+Inputs are seeded synthetic workloads, resident in HBM before timing. The
+KV cache is replicated so consecutive steps read different copies (>= 1 GiB
+in rotation), so no step finds the previous step's pages in the 256 MB
+last-level cache.
+
+Prints one JSON line per workload (default: the memory-bound workload).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from workloads import (MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, algorithmic_bytes,  # noqa: E402
+                       algorithmic_flops, make_workload_inputs)
+
+METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
+DEFAULT_WORKLOAD = "memory_bound"
+KERNEL_SOURCES = ["mla_decode_kernel.hip", "mla_combine_kernel.hip", "mla_common.h", "mla_sched.h",
+                  "mla_api.cpp", "mla_internal.h", "mla_sched_kernel.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_paged_kv_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 counter runs,
+    or None when absent or taken on different kernel sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            doc = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = doc.get("workloads", {}).get(workload)
+    if not entry or entry.get("kernel_digest") != kernel_digest():
+        return None
+    return entry.get("bytes_per_call")
+
+
+def cpu_baseline(workload: str, inp, budget_s: float):
+    """The FP64 oracle, untuned, on a bounded sample of the same workload:
+    whole sequences in order until ~budget_s of CPU time. Reported in the
+    workload's algorithmic GB/s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    w = WORKLOADS[workload]
+    t0 = time.perf_counter()
+    done = []
+    for b in range(inp.batch):
+        oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale,
+                              inp.causal, seqs=[b])
+        done.append(b)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    nbytes = algorithmic_bytes(inp.seqlens[done], w.s_q, w.h_q)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {len(done)} of {inp.batch} sequences ({int(inp.seqlens[done].sum())} "
+                      f"tokens), {dt:.1f} s, numpy FP64 two-pass softmax per sequence"}
+
+
+def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_bytes: int,
+                 num_partitions: int = 0):
+    import torch
+    import mla_paged_kv_02_amd as mla
+
+    w = WORKLOADS[name]
+    inp = make_workload_inputs(name)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    kv0 = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seqlens).to(dev)
+    kv_bytes = kv0.numel() * 2
+    copies = max(1, min(16, math.ceil(rotate_bytes / max(kv_bytes, 1))))
+    kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
+    out = torch.empty((inp.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, w.s_q, w.h_q), dtype=torch.float32, device=dev)
+    ws = torch.empty(mla.workspace_bytes(inp.batch, w.h_q, w.s_q, num_partitions),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions)
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode_fwd(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out,
+                       lse=lse, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / steps
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    call_ms_mean = float(call_ms.mean())
+
+    nbytes = algorithmic_bytes(inp.seqlens, w.s_q, w.h_q)
+    flops = algorithmic_flops(inp.seqlens, w.s_q, w.h_q, w.causal)
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    call_gbps = nbytes / (call_ms_mean * 1e-3) / 1e9
+    call_tflops = flops / (call_ms_mean * 1e-3) / 1e12
+    hbm_bound = nbytes * 1.0 / (MI355X_HBM_GBPS * 1e9) >= flops * 1.0 / (MI355X_BF16_TFLOPS * 1e12)
+    traffic = counter_traffic(name)
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": MI355X_HBM_GBPS,
+                "unit": "GB/s", "frac": round(call_gbps / MI355X_HBM_GBPS, 4),
+                "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(call_tflops, 2), "peak": MI355X_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(call_tflops / MI355X_BF16_TFLOPS, 4),
+                "traffic": traffic}
+    line = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; BF16 N(0,1) query and cache, shuffled block table)",
+        "config": {"workload": f"{name}: {w.description}, d=576, dv=512, page 64, "
+                               f"{'causal' if w.causal else 'non-causal'}",
+                   "batch": inp.batch, "s_q": w.s_q, "h_q": w.h_q,
+                   "total_tokens": int(inp.seqlens.sum()), "seed": w.seed},
+        "tflops": round(tflops, 2),
+        "hbm_frac_of_peak": round(gbps / MI355X_HBM_GBPS, 4),
+        "mfma_frac_of_peak": round(tflops / MI355X_BF16_TFLOPS, 4),
+        "decode_call_us": round(call_ms_mean * 1e3, 2),
+        "decode_call_us_min": round(float(call_ms.min()) * 1e3, 2),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+        "kv_copies_rotated": copies,
+        "roofline": roof,
+        "kernel_digest": kernel_digest(),
+    }
+    if cpu_budget > 0:
+        line["cpu_baseline"] = cpu_baseline(name, inp, cpu_budget)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="one of %s, or 'all'" % ", ".join(WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
+    ap.add_argument("--rotate-gib", type=float, default=1.0)
+    ap.add_argument("--num-partitions", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    for name in names:
+        line = run_workload(name, args.steps, args.warmup,
+                            args.cpu_budget if name == DEFAULT_WORKLOAD or args.workload != "all" else 0,
+                            int(args.rotate_gib * (1 << 30)), args.num_partitions)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

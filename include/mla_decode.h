@@ -1,0 +1,168 @@
+/*
+ * mla_decode.h - C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * What it computes. Multi-head Latent Attention decode over a paged,
+ * compressed KV cache, as described on the FlashMLA overview page
+ * (nullthought.net, "FlashMLA Overview": BF16, a paged KV cache with 64-token
+ * blocks, variable-length sequences) and on the page "MLA 和 MHA 的 Kernel
+ * 区别" (MLA vs MHA kernel differences), sections "内存布局和 KV Cache 大小"
+ * (the cache holds only the latent c_KV) and "Decode 阶段的 HBM 访问模式" /
+ * "MLA Decode" (score every cached token, softmax, weighted sum of values).
+ *
+ * The query arrives in absorbed form (W_UK folded in), so each cache row of
+ * 576 BF16 values is the key, and its first 512 values are the value. The
+ * last 64 values are a pre-rotated positional part that enters scores only.
+ * For sequence b, query token i and head h (row r = i*h_q + h):
+ *
+ *   L      = N_b                         (causal == 0)
+ *          = clamp(N_b - s_q + i + 1, 0, N_b)   (causal == 1)
+ *   s_t    = softmax_scale * <q[b,i,h,:], K_t>,   t < L
+ *   out    = sum_t softmax(s)_t * K_t[0:512]      (BF16, round to nearest even)
+ *   lse    = ln sum_t exp(s_t)                    (FP32; -inf when L == 0)
+ *
+ * where K_t is row t mod 64 of physical page block_table[b][t / 64]. A row
+ * with L == 0 outputs zeros.
+ *
+ * Calling pattern (FlashMLA overview page, flash_api.cpp walk-through: the
+ * metadata call is made once, then the attention call once per layer):
+ *
+ *   once per decode step:  mla_get_split_metadata(...)
+ *   once per layer:        mla_decode_fwd(...)
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are device memory on the current HIP device;
+ *    "host" pointers are ordinary host memory. The caller owns every buffer;
+ *    the library keeps no per-call state and allocates nothing.
+ *  - `stream` is a hipStream_t (NULL = the default stream). All device work
+ *    is enqueued on it; no call synchronises the host.
+ *  - Arguments are validated on the host before any HIP call. A failed check
+ *    returns a status and enqueues nothing. Exceptions never cross the ABI.
+ *  - Conditions that cannot be checked without reading device memory are
+ *    preconditions (listed per call); breaking them is undefined behaviour.
+ *  - Calls on different streams may run concurrently as long as they do not
+ *    share workspace or metadata buffers.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed geometry: one latent KV head, rows of 576 BF16 (512 latent + 64
+ * positional), values = first 512 entries, pages of 64 tokens. */
+#define MLA_HEAD_DIM 576
+#define MLA_HEAD_DIM_V 512
+#define MLA_PAGE_SIZE 64
+/* Largest supported rows per sequence, M = h_q * s_q. */
+#define MLA_MAX_ROWS 1024
+
+typedef enum mla_status {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,          /* null pointer, bad size, bad flag        */
+    MLA_ERR_UNSUPPORTED = 2,          /* shape outside what the kernels cover   */
+    MLA_ERR_MISALIGNED = 3,           /* pointer alignment requirement broken   */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 4,  /* metadata or workspace buffer too small */
+    MLA_ERR_HIP = 5                   /* a HIP runtime call or launch failed    */
+} mla_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(int status);
+
+/* ABI version of this header, (major << 16) | minor. */
+int mla_abi_version(void);
+
+/* Number of partitions the split scheduler uses by default for this shape on
+ * the current device (a function of the device's compute-unit count and of
+ * M = h_q * s_q). Returns <= 0 with no device. Host-only query. */
+int mla_default_num_partitions(int h_q, int s_q);
+
+/* Bytes of the metadata buffer for `batch` sequences and `num_partitions`
+ * partitions (num_partitions <= 0 means the default). 0 on invalid input. */
+size_t mla_metadata_bytes(int batch, int h_q, int s_q, int num_partitions);
+
+/* Bytes of scratch workspace mla_decode_fwd needs (split partial results, and
+ * the metadata when the call computes it itself). 0 on invalid input. */
+size_t mla_workspace_bytes(int batch, int h_q, int s_q, int num_partitions);
+
+/*
+ * mla_get_split_metadata - split-KV work plan for one decode step.
+ *
+ * The work of a step is the list of (sequence, page) pairs. It is cut into
+ * `num_partitions` contiguous ranges of near-equal cost (a range may start or
+ * end inside a sequence; a sequence cut into several ranges is recombined by
+ * its log-sum-exp). This spreads small-batch, long-context decode over all
+ * compute units (motivation: the long-text inference page, "Unlocking GPU
+ * Potential ...", on decode starving the GPU when batch < SM count).
+ * The plan depends only on seqlens, h_q, s_q and num_partitions, so it can be
+ * reused by every layer of the step.
+ *
+ *   seqlens         device int32[batch], N_b >= 0 (cached tokens per sequence,
+ *                   including the s_q new ones)
+ *   batch           >= 1
+ *   h_q, s_q        query heads (>= 1) and new tokens per sequence (>= 1);
+ *                   h_q * s_q <= MLA_MAX_ROWS
+ *   num_partitions  <= 0 for the default, else 1..65536
+ *   metadata        device int32 buffer, 4-byte aligned, of at least
+ *                   mla_metadata_bytes(batch, h_q, s_q, num_partitions) bytes;
+ *                   written by the call
+ *   stream          hipStream_t
+ *
+ * Precondition: total pages sum_b ceil(N_b/64) < 2^30.
+ */
+mla_status mla_get_split_metadata(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                  int num_partitions, int32_t* metadata,
+                                  size_t metadata_bytes, void* stream);
+
+/*
+ * Same plan computed on the host from host seqlens into a host buffer of the
+ * same layout (for callers that already hold lengths on the host, and for
+ * tests). Uses no GPU.
+ */
+mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                       int num_partitions, int32_t* metadata,
+                                       size_t metadata_bytes);
+
+/*
+ * mla_decode_fwd - MLA decode attention for one layer (see top of file).
+ *
+ *   q              device bf16 [batch][s_q][h_q][576], contiguous, 16-byte aligned
+ *   kv_cache       device bf16 [num_pages][64][1][576], contiguous, 16-byte aligned
+ *   block_table    device int32 [batch][max_blocks_per_seq], 4-byte aligned
+ *   max_blocks_per_seq  row stride of block_table, >= 1
+ *   seqlens        device int32 [batch]
+ *   batch, s_q, h_q     as for mla_get_split_metadata (must match it)
+ *   num_pages      number of physical pages in kv_cache, >= 1
+ *   softmax_scale  finite, > 0 (e.g. 1/sqrt(576))
+ *   causal         0 or 1 (bottom-right mask over the s_q new tokens)
+ *   metadata       device buffer from mla_get_split_metadata for the same
+ *                  seqlens/batch/h_q/s_q/num_partitions, or NULL to have this
+ *                  call compute it inside `workspace` first
+ *   num_partitions the value given to mla_get_split_metadata (<= 0: default)
+ *   workspace      device scratch, 16-byte aligned, of at least
+ *                  mla_workspace_bytes(batch, h_q, s_q, num_partitions) bytes;
+ *                  contents on entry are ignored
+ *   out            device bf16 [batch][s_q][h_q][512], 16-byte aligned (written)
+ *   lse            device fp32 [batch][s_q][h_q], 4-byte aligned (written)
+ *   stream         hipStream_t
+ *
+ * Preconditions: 0 <= block_table[b][n] < num_pages for n < ceil(N_b/64);
+ * N_b <= 64 * max_blocks_per_seq. Entries past a sequence's last page and
+ * page rows past N_b are never used and may hold anything (NaN included).
+ * Buffers must not overlap, except q/kv_cache/block_table/seqlens which are
+ * only read.
+ */
+mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
+                          int h_q, int num_pages, float softmax_scale, int causal,
+                          const int32_t* metadata, int num_partitions, void* workspace,
+                          size_t workspace_bytes, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

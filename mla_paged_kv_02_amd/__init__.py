@@ -1,0 +1,168 @@
+"""MLA paged decode on MI355X (gfx950): Python binding of libmla_decode.so.
+
+Two calls, as on the FlashMLA overview page (flash_api.cpp walk-through):
+the split metadata once per decode step, then the attention call once per
+layer.
+
+    meta = get_split_metadata(seqlens, h_q, s_q)
+    out, lse = decode_fwd(q, kv_cache, block_table, seqlens, scale, causal, meta=meta)
+
+This module only checks and marshals arguments; every step of the
+computation runs in the library's HIP kernels. torch provides device memory
+and the current stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import MlaError, check, lib  # noqa: F401
+
+HEAD_DIM = 576
+HEAD_DIM_V = 512
+PAGE_SIZE = 64
+
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "split_metadata_host",
+           "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype, device=None, ndim=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def metadata_bytes(batch: int, h_q: int, s_q: int, num_partitions: int = 0) -> int:
+    return int(lib().mla_metadata_bytes(batch, h_q, s_q, num_partitions))
+
+
+def workspace_bytes(batch: int, h_q: int, s_q: int, num_partitions: int = 0) -> int:
+    return int(lib().mla_workspace_bytes(batch, h_q, s_q, num_partitions))
+
+
+def default_num_partitions(h_q: int, s_q: int) -> int:
+    return int(lib().mla_default_num_partitions(h_q, s_q))
+
+
+@dataclasses.dataclass
+class SplitMeta:
+    """Split-KV plan of one decode step (device buffer plus the arguments it
+    was built for). Reuse it for every layer of the step."""
+
+    metadata: torch.Tensor
+    batch: int
+    h_q: int
+    s_q: int
+    num_partitions: int
+
+
+def get_split_metadata(seqlens: torch.Tensor, h_q: int, s_q: int,
+                       num_partitions: int = 0) -> SplitMeta:
+    """Build the split plan on the device, on the current stream."""
+    _require(seqlens, "seqlens", torch.int32, ndim=1)
+    batch = seqlens.shape[0]
+    nbytes = metadata_bytes(batch, h_q, s_q, num_partitions)
+    if nbytes == 0:
+        raise ValueError(f"unsupported shape batch={batch} h_q={h_q} s_q={s_q}")
+    meta = torch.empty(nbytes // 4, dtype=torch.int32, device=seqlens.device)
+    check(lib().mla_get_split_metadata(seqlens.data_ptr(), batch, h_q, s_q, num_partitions,
+                                       meta.data_ptr(), nbytes, _stream_ptr(seqlens.device)),
+          "mla_get_split_metadata")
+    return SplitMeta(meta, batch, h_q, s_q, num_partitions)
+
+
+def split_metadata_host(seqlens, h_q: int, s_q: int, num_partitions: int) -> np.ndarray:
+    """The same plan computed on the host (no GPU), as an int32 array."""
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    batch = sl.shape[0]
+    nbytes = metadata_bytes(batch, h_q, s_q, num_partitions)
+    if nbytes == 0:
+        raise ValueError("unsupported shape")
+    meta = np.zeros(nbytes // 4, dtype=np.int32)
+    check(lib().mla_get_split_metadata_host(sl.ctypes.data, batch, h_q, s_q, num_partitions,
+                                            meta.ctypes.data, nbytes),
+          "mla_get_split_metadata_host")
+    return meta
+
+
+def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+               seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+               meta: Optional[SplitMeta] = None, out: Optional[torch.Tensor] = None,
+               lse: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None,
+               num_partitions: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MLA decode attention for one layer.
+
+    q [B, s_q, h_q, 576] bf16; kv_cache [num_pages, 64, 1, 576] (or
+    [num_pages, 64, 576]) bf16; block_table [B, max_blocks] int32;
+    seqlens [B] int32. Returns out [B, s_q, h_q, 512] bf16 and
+    lse [B, s_q, h_q] float32. Without ``meta`` the call builds the plan
+    itself inside its workspace.
+    """
+    dev = q.device
+    _require(q, "q", torch.bfloat16, ndim=4)
+    bsz, s_q, h_q, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError(f"q head dim must be {HEAD_DIM}, got {d}")
+    _require(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    if kv_cache.dim() == 4:
+        if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, 1, HEAD_DIM):
+            raise ValueError(f"kv_cache must be [num_pages, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    elif kv_cache.dim() == 3:
+        if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, HEAD_DIM):
+            raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
+    else:
+        raise ValueError("kv_cache must have 3 or 4 dims")
+    _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
+    _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != bsz or seqlens.shape[0] != bsz:
+        raise ValueError("block_table and seqlens must have one row per sequence")
+    if meta is not None:
+        if (meta.batch, meta.h_q, meta.s_q) != (bsz, h_q, s_q):
+            raise ValueError("meta was built for a different batch/h_q/s_q")
+        num_partitions = meta.num_partitions
+    if out is None:
+        out = torch.empty((bsz, s_q, h_q, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+    else:
+        _require(out, "out", torch.bfloat16, device=dev, ndim=4)
+        if tuple(out.shape) != (bsz, s_q, h_q, HEAD_DIM_V):
+            raise ValueError("out has the wrong shape")
+    if lse is None:
+        lse = torch.empty((bsz, s_q, h_q), dtype=torch.float32, device=dev)
+    else:
+        _require(lse, "lse", torch.float32, device=dev, ndim=3)
+        if tuple(lse.shape) != (bsz, s_q, h_q):
+            raise ValueError("lse has the wrong shape")
+    need = workspace_bytes(bsz, h_q, s_q, num_partitions)
+    if need == 0:
+        raise ValueError(f"unsupported shape B={bsz} h_q={h_q} s_q={s_q}")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous buffer of >= {need} bytes")
+    status = lib().mla_decode_fwd(
+        q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1],
+        seqlens.data_ptr(), bsz, s_q, h_q, kv_cache.shape[0], ctypes.c_float(softmax_scale),
+        int(bool(causal)), meta.metadata.data_ptr() if meta is not None else None,
+        num_partitions, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
+    check(status, "mla_decode_fwd")
+    return out, lse

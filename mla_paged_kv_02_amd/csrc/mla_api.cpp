@@ -1,0 +1,254 @@
+// mla_api.cpp - the C ABI (include/mla_decode.h): argument checks, the work
+// plan, and the launches. The caller-facing steps follow the FlashMLA
+// overview page (flash_api.cpp walk-through): compute the split metadata once
+// per decode step, then run the attention call once per layer; the bridge
+// checks its inputs and orchestrates the kernels.
+#include "../../include/mla_decode.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "mla_common.h"
+#include "mla_internal.h"
+#include "mla_sched.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+// Compute units of the current device (0 if none).
+int current_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    std::call_once(g_cu_once[dev], [dev]() {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            n = 0;
+        }
+        g_cu_count[dev] = n;
+    });
+    return g_cu_count[dev];
+}
+
+// Optional override of the rows per workgroup (16, 32 or 64), read once.
+int tile_rows_override() {
+    static int v = []() {
+        const char* e = std::getenv("MLA_TILE_ROWS");
+        if (!e) return 0;
+        int t = std::atoi(e);
+        return (t == 16 || t == 32 || t == 64) ? t : 0;
+    }();
+    return v;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan) {
+    if (batch < 1 || h_q < 1 || s_q < 1) return false;
+    const long long m = (long long)h_q * s_q;
+    if (m > MLA_MAX_ROWS) return false;
+    if (num_partitions > 65536) return false;
+    Plan pl{};
+    pl.batch = batch;
+    pl.h_q = h_q;
+    pl.s_q = s_q;
+    pl.M = (int)m;
+    int tm = tile_rows_override();
+    if (tm == 0) tm = pl.M <= 16 ? 16 : pl.M <= 32 ? 32 : 64;
+    pl.tm = tm;
+    // 4 waves of 16 query rows; waves sharing rows split the 512 value columns
+    pl.nw = 4;
+    pl.nc = 64 / tm;
+    pl.R = (pl.M + tm - 1) / tm;
+    int p = num_partitions;
+    if (p <= 0) {
+        const int cus = num_cus > 0 ? num_cus : 256;
+        p = cus / pl.R;
+        if (p < 1) p = 1;
+    }
+    pl.P = (p + 7) / 8 * 8;  // whole groups of 8 for the XCD-aware block mapping
+    // fixed cost of a segment in page units: the pipeline fill of its first
+    // page plus query load and output or partial traffic (~5 KB per row)
+    pl.cseg = 1 + tm / 16;
+    pl.slots = 2 * pl.P;
+    *plan = pl;
+    return true;
+}
+
+size_t metadata_bytes(const Plan& plan) { return (size_t)meta_ints(plan.batch, plan.P) * 4; }
+
+WorkspaceLayout workspace_layout(const Plan& plan, bool with_metadata) {
+    WorkspaceLayout w{};
+    w.meta_off = 0;
+    w.meta_bytes = with_metadata ? align_up(metadata_bytes(plan), 256) : 0;
+    w.lse_off = w.meta_off + w.meta_bytes;
+    w.lse_bytes = align_up((size_t)plan.slots * plan.M * sizeof(float), 256);
+    w.o_off = w.lse_off + w.lse_bytes;
+    w.o_bytes = (size_t)plan.slots * plan.M * MLA_HEAD_DIM_V * sizeof(float);
+    w.total = w.o_off + w.o_bytes;
+    return w;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+    switch (status) {
+        case MLA_OK: return "MLA_OK";
+        case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+        case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: unsupported shape";
+        case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED: pointer alignment";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: buffer too small";
+        case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+        default: return "MLA_ERR_UNKNOWN";
+    }
+}
+
+int mla_abi_version(void) { return (1 << 16) | 0; }
+
+int mla_default_num_partitions(int h_q, int s_q) {
+    const int cus = current_cu_count();
+    if (cus <= 0) return 0;
+    Plan pl;
+    if (!make_plan(1, h_q, s_q, 0, cus, &pl)) return 0;
+    return pl.P;
+}
+
+size_t mla_metadata_bytes(int batch, int h_q, int s_q, int num_partitions) {
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions,
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+        return 0;
+    return metadata_bytes(pl);
+}
+
+size_t mla_workspace_bytes(int batch, int h_q, int s_q, int num_partitions) {
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions,
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+        return 0;
+    return workspace_layout(pl, true).total;
+}
+
+static mla_status check_meta_args(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                  int num_partitions, const int32_t* metadata) {
+    if (!seqlens || !metadata) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || h_q < 1 || s_q < 1 || num_partitions > 65536) return MLA_ERR_INVALID_ARG;
+    if ((long long)h_q * s_q > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+    if (!aligned(seqlens, 4) || !aligned(metadata, 4)) return MLA_ERR_MISALIGNED;
+    return MLA_OK;
+}
+
+mla_status mla_get_split_metadata(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                  int num_partitions, int32_t* metadata, size_t metadata_bytes_,
+                                  void* stream) {
+    mla_status st = check_meta_args(seqlens, batch, h_q, s_q, num_partitions, metadata);
+    if (st != MLA_OK) return st;
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions,
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+        return MLA_ERR_UNSUPPORTED;
+    if (metadata_bytes_ < metadata_bytes(pl)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, metadata,
+                              reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                       int num_partitions, int32_t* metadata,
+                                       size_t metadata_bytes_) {
+    mla_status st = check_meta_args(seqlens, batch, h_q, s_q, num_partitions, metadata);
+    if (st != MLA_OK) return st;
+    for (int b = 0; b < batch; ++b)
+        if (seqlens[b] < 0) return MLA_ERR_INVALID_ARG;
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions,
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+        return MLA_ERR_UNSUPPORTED;
+    if (metadata_bytes_ < metadata_bytes(pl)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    split_metadata_host(seqlens, batch, pl.P, pl.cseg, metadata);
+    return MLA_OK;
+}
+
+mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
+                          int h_q, int num_pages, float softmax_scale, int causal,
+                          const int32_t* metadata, int num_partitions, void* workspace,
+                          size_t workspace_bytes_, void* out, float* lse, void* stream) {
+    if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse)
+        return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || s_q < 1 || h_q < 1 || max_blocks_per_seq < 1 || num_pages < 1)
+        return MLA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (num_partitions > 65536) return MLA_ERR_INVALID_ARG;
+    if ((long long)h_q * s_q > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * batch > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+        return MLA_ERR_MISALIGNED;
+    if (!aligned(block_table, 4) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
+        (metadata && !aligned(metadata, 4)))
+        return MLA_ERR_MISALIGNED;
+
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions,
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+        return MLA_ERR_UNSUPPORTED;
+    const WorkspaceLayout wl = workspace_layout(pl, metadata == nullptr);
+    if (workspace_bytes_ < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int32_t* meta = metadata;
+    if (!meta) {
+        int32_t* m = reinterpret_cast<int32_t*>(ws + wl.meta_off);
+        if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, m, st) != hipSuccess)
+            return MLA_ERR_HIP;
+        meta = m;
+    }
+
+    DecodeArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.kv = static_cast<const uint16_t*>(kv_cache);
+    a.block_table = block_table;
+    a.seqlens = seqlens;
+    a.meta = meta;
+    a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+    a.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.max_blocks = max_blocks_per_seq;
+    a.batch = batch;
+    a.s_q = s_q;
+    a.h_q = h_q;
+    a.M = pl.M;
+    a.R = pl.R;
+    a.P = pl.P;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.causal = causal;
+    if (launch_decode(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
+    if (launch_combine(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+}  // extern "C"

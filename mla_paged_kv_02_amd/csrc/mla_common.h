@@ -1,0 +1,79 @@
+// mla_common.h - gfx950 device helpers shared by the decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+#define MLA_AS1 __attribute__((address_space(1)))
+#define MLA_AS3 __attribute__((address_space(3)))
+
+constexpr int kHeadDim = 576;
+constexpr int kHeadDimV = 512;
+constexpr int kRowBytes = kHeadDim * 2;          // 1152 B per cache row
+constexpr int kPageRows = 64;
+constexpr int kPageBytes = kPageRows * kRowBytes;  // 73728 B per page
+constexpr int kRowChunks = kRowBytes / 16;       // 72 16-byte chunks per row
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// LDS placement of a page row. A row is 1152 B, a multiple of the bank
+// period, so the same column of consecutive rows would hit the same banks.
+// Chunk c (16 B) of row r is stored at chunk slot c ^ swz(r); the XOR only
+// touches the low three bits, so a slot stays inside its aligned group of 8
+// and inside the 72-chunk row.
+__device__ __forceinline__ int lds_swizzle(int row) { return row & 7; }
+
+__device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4);
+}
+
+// One 16-row x 16-column x 32-deep BF16 product, FP32 accumulate.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_read16(const uint8_t* p) {
+    return *reinterpret_cast<const MLA_AS3 bf16x8*>(
+        reinterpret_cast<const MLA_AS3 uint8_t*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Transposing LDS read: in each group of 16 lanes, lane i addresses row i/4,
+// elements 4*(i%4)..+3 of a 4 x 16 block of 16-bit values and receives column
+// i of that block (its 4 rows).
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<MLA_AS3 bf16x4*>(
+        reinterpret_cast<MLA_AS3 uint8_t*>(reinterpret_cast<uintptr_t>(p))));
+}
+
+// 16-byte direct load from global memory into LDS. Every lane of the wave
+// supplies its own source; the wave's 64 chunks land contiguously at `lds_dst`
+// (lane k at byte 16*k), which must be the same for all lanes.
+__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
+    __builtin_amdgcn_global_load_lds(
+        reinterpret_cast<const MLA_AS1 void*>(reinterpret_cast<uintptr_t>(src)),
+        reinterpret_cast<MLA_AS3 void*>(reinterpret_cast<uintptr_t>(lds_dst)), 16, 0, 0);
+}
+
+__device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
+    bf16x8 r;
+    r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
+    r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 cat_bf16x4(bf16x4 lo, bf16x4 hi) {
+    bf16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+}  // namespace mla

@@ -1,0 +1,62 @@
+// mla_internal.h - host-side plan and kernel launchers (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// How one decode call is cut into workgroups.
+//   rows per workgroup (tm) = 16 * waves / column groups
+//   every wave owns 16 query rows and 512/nc value columns
+//   R row blocks cover the M = h_q*s_q rows of a sequence; P partitions cut
+//   the page list; the grid is P*R workgroups.
+struct Plan {
+    int batch, h_q, s_q, M;
+    int tm, nw, nc;
+    int R, P;
+    int cseg;
+    int slots;  // capacity of the split-partial buffers (sequence splits)
+};
+
+// Returns false for unsupported shapes. num_partitions <= 0 selects the default.
+bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan);
+
+// Byte layout of the workspace: [metadata (optional)] [partial lse] [partial O].
+struct WorkspaceLayout {
+    size_t meta_off, meta_bytes;
+    size_t lse_off, lse_bytes;
+    size_t o_off, o_bytes;
+    size_t total;
+};
+WorkspaceLayout workspace_layout(const Plan& plan, bool with_metadata);
+size_t metadata_bytes(const Plan& plan);
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* kv;
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    const int32_t* meta;
+    float* part_o;
+    float* part_lse;
+    uint16_t* out;
+    float* lse;
+    int max_blocks;
+    int batch, s_q, h_q, M;
+    int R, P;
+    float scale_log2;  // softmax_scale * log2(e)
+    int causal;
+};
+
+hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_partitions, int cseg,
+                                 int32_t* meta, hipStream_t stream);
+hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+
+// Host build of the same plan (tests and host callers).
+void split_metadata_host(const int32_t* seqlens, int batch, int num_partitions, int cseg,
+                         int32_t* meta);
+
+}  // namespace mla

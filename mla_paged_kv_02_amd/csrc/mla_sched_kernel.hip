@@ -1,0 +1,146 @@
+// mla_sched_kernel.hip - builds the split-KV plan (see mla_sched.h) on the
+// device in one workgroup, and the identical plan on the host.
+#include "mla_internal.h"
+#include "mla_sched.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kSchedThreads = 1024;
+
+// Exclusive prefix sum over the workgroup; *total receives the sum.
+__device__ int block_exclusive_scan(int v, int* total) {
+    __shared__ int wave_sums[kSchedThreads / 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += t;
+    }
+    if (lane == 63) wave_sums[wave] = incl;
+    __syncthreads();
+    int offset = 0, sum = 0;
+    for (int w = 0; w < kSchedThreads / 64; ++w) {
+        const int ws = wave_sums[w];
+        if (w < wave) offset += ws;
+        sum += ws;
+    }
+    __syncthreads();
+    *total = sum;
+    return offset + incl - v;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int32_t* seqlens,
+                                                                       int batch, int P, int cseg,
+                                                                       int32_t* meta) {
+    int32_t* seq = meta + kMetaHeader + 4 * P;
+    const int tid = threadIdx.x;
+
+    // cost-line start of every sequence
+    int carry = 0;
+    for (int base = 0; base < batch; base += kSchedThreads) {
+        const int b = base + tid;
+        const int v = b < batch ? (int)cost_len(seqlens[b], cseg) : 0;
+        int chunk_total;
+        const int ex = block_exclusive_scan(v, &chunk_total);
+        if (b < batch) seq[4 * b + 3] = carry + ex;
+        carry += chunk_total;
+    }
+    const int64_t total = carry;
+    const int32_t pa = active_partitions(total, P);
+
+    // partitions holding each sequence's pages; split-partial slots
+    int slots = 0;
+    for (int base = 0; base < batch; base += kSchedThreads) {
+        const int b = base + tid;
+        int first = -1, count = 0;
+        if (b < batch) seq_partitions(seq[4 * b + 3], pages_of(seqlens[b]), cseg, total, pa, &first, &count);
+        const int v = count > 1 ? count : 0;
+        int chunk_total;
+        const int ex = block_exclusive_scan(v, &chunk_total);
+        if (b < batch) {
+            seq[4 * b + 0] = count > 1 ? slots + ex : -1;
+            seq[4 * b + 1] = first;
+            seq[4 * b + 2] = count;
+        }
+        slots += chunk_total;
+    }
+    __syncthreads();
+
+    // partition boundaries
+    for (int p = tid; p < P; p += kSchedThreads) {
+        int32_t* e = meta + kMetaHeader + 4 * p;
+        if (p < pa) {
+            boundary_at(partition_start(p, total, pa), seq + 3, 4, batch, total, cseg, &e[0], &e[1]);
+            boundary_at(partition_start(p + 1, total, pa), seq + 3, 4, batch, total, cseg, &e[2], &e[3]);
+        } else {
+            e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
+        }
+    }
+    if (tid < kMetaHeader) {
+        int32_t h = 0;
+        switch (tid) {
+            case 0: h = kMetaMagic; break;
+            case 1: h = batch; break;
+            case 2: h = P; break;
+            case 3: h = cseg; break;
+            case 4: h = pa > 0 ? (int32_t)((total + pa - 1) / pa) : 0; break;
+            case 5: h = slots; break;
+            case 6: h = (int32_t)total; break;
+            case 7: h = pa; break;
+            default: h = 0;
+        }
+        meta[tid] = h;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_partitions, int cseg,
+                                 int32_t* meta, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_split_meta_kernel, dim3(1), dim3(kSchedThreads), 0, stream, seqlens,
+                       batch, num_partitions, cseg, meta);
+    return hipGetLastError();
+}
+
+void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int32_t* meta) {
+    int32_t* seq = meta + kMetaHeader + 4 * P;
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) {
+        seq[4 * b + 3] = (int32_t)total;
+        total += cost_len(seqlens[b], cseg);
+    }
+    const int32_t pa = active_partitions(total, P);
+    int slots = 0;
+    for (int b = 0; b < batch; ++b) {
+        int first, count;
+        seq_partitions(seq[4 * b + 3], pages_of(seqlens[b]), cseg, total, pa, &first, &count);
+        seq[4 * b + 0] = count > 1 ? slots : -1;
+        seq[4 * b + 1] = first;
+        seq[4 * b + 2] = count;
+        if (count > 1) slots += count;
+    }
+    for (int p = 0; p < P; ++p) {
+        int32_t* e = meta + kMetaHeader + 4 * p;
+        if (p < pa) {
+            boundary_at(partition_start(p, total, pa), seq + 3, 4, batch, total, cseg, &e[0], &e[1]);
+            boundary_at(partition_start(p + 1, total, pa), seq + 3, 4, batch, total, cseg, &e[2], &e[3]);
+        } else {
+            e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
+        }
+    }
+    for (int i = 0; i < kMetaHeader; ++i) meta[i] = 0;
+    meta[0] = kMetaMagic;
+    meta[1] = batch;
+    meta[2] = P;
+    meta[3] = cseg;
+    meta[4] = pa > 0 ? (int32_t)((total + pa - 1) / pa) : 0;
+    meta[5] = slots;
+    meta[6] = (int32_t)total;
+    meta[7] = pa;
+}
+
+}  // namespace mla

@@ -1,0 +1,101 @@
+"""The C ABI on the host (no GPU): the library loads, exports every entry
+point the header declares, and rejects bad arguments with the documented
+status before making any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_paged_kv_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, TOO_SMALL, HIP = range(6)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_two_calls():
+    names = declared_functions()
+    assert "mla_get_split_metadata" in names and "mla_decode_fwd" in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} missing from libmla_decode.so"
+        assert name in _lib.SIGNATURES, f"{name} has no binding signature"
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for code in range(6):
+        assert lib.mla_status_string(code).decode().startswith(_lib.STATUS_NAMES[code])
+    assert lib.mla_abi_version() >> 16 == 1
+
+
+def test_size_queries():
+    lib = _lib.lib()
+    assert lib.mla_metadata_bytes(0, 16, 1, 64) == 0          # batch < 1
+    assert lib.mla_metadata_bytes(4, 0, 1, 64) == 0           # h_q < 1
+    assert lib.mla_metadata_bytes(4, 512, 4, 64) == 0         # M > MLA_MAX_ROWS
+    assert lib.mla_metadata_bytes(4, 16, 1, 64) == 4 * (16 + 4 * 64 + 4 * 4)
+    assert lib.mla_metadata_bytes(4, 16, 1, 60) == 4 * (16 + 4 * 64 + 4 * 4)  # rounded to 8
+    ws = lib.mla_workspace_bytes(4, 16, 1, 64)
+    assert ws >= 2 * 64 * 16 * 512 * 4
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+def _decode(**kw):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, maxb=4, seqlens=FAKE, batch=2, s_q=1, h_q=16,
+                pages=8, scale=1 / 24, causal=0, meta=FAKE, nparts=64, ws=FAKE,
+                ws_bytes=1 << 30, out=FAKE, lse=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_decode_fwd(
+        args["q"], args["kv"], args["bt"], args["maxb"], args["seqlens"], args["batch"],
+        args["s_q"], args["h_q"], args["pages"], ctypes.c_float(args["scale"]), args["causal"],
+        args["meta"], args["nparts"], args["ws"], args["ws_bytes"], args["out"], args["lse"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kv=None), INVALID), (dict(bt=None), INVALID),
+    (dict(seqlens=None), INVALID), (dict(ws=None), INVALID), (dict(out=None), INVALID),
+    (dict(lse=None), INVALID), (dict(batch=0), INVALID), (dict(s_q=0), INVALID),
+    (dict(h_q=0), INVALID), (dict(maxb=0), INVALID), (dict(pages=0), INVALID),
+    (dict(causal=2), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(nparts=70000), INVALID),
+    (dict(h_q=128, s_q=16), UNSUPPORTED),
+    (dict(q=FAKE + 8), MISALIGNED), (dict(kv=FAKE + 4), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
+    (dict(ws=FAKE + 8), MISALIGNED), (dict(bt=FAKE + 2), MISALIGNED), (dict(lse=FAKE + 1), MISALIGNED),
+    (dict(seqlens=FAKE + 3), MISALIGNED), (dict(meta=FAKE + 2), MISALIGNED),
+    (dict(ws_bytes=1024), TOO_SMALL),
+])
+def test_decode_argument_checks(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_metadata_argument_checks():
+    lib = _lib.lib()
+    assert lib.mla_get_split_metadata(None, 2, 16, 1, 64, FAKE, 1 << 20, None) == INVALID
+    assert lib.mla_get_split_metadata(FAKE, 0, 16, 1, 64, FAKE, 1 << 20, None) == INVALID
+    assert lib.mla_get_split_metadata(FAKE, 2, 16, 1, 64, FAKE + 2, 1 << 20, None) == MISALIGNED
+    assert lib.mla_get_split_metadata(FAKE, 2, 1024, 2, 64, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.mla_get_split_metadata(FAKE, 2, 16, 1, 64, FAKE, 16, None) == TOO_SMALL
+
+
+def test_host_metadata_rejects_negative_lengths():
+    import numpy as np
+    sl = np.array([5, -1], dtype=np.int32)
+    meta = np.zeros(4096, dtype=np.int32)
+    st = _lib.lib().mla_get_split_metadata_host(sl.ctypes.data, 2, 16, 1, 8, meta.ctypes.data, meta.nbytes)
+    assert st == INVALID

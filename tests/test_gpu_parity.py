@@ -1,0 +1,141 @@
+"""HIP path vs the FP64 oracle, element by element, through the C ABI.
+
+Small cases span several pages, ragged tails, empty sequences, the causal
+mask and forced splits; the named workloads run at full size and are
+compared on sampled sequences the oracle computes one by one.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, run_decode, score
+from workloads import (WORKLOADS, make_inputs, make_workload_inputs, permute_pages,
+                       poison_block_table_padding, poison_page_tails)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(inp, num_partitions=0, seqs=None, use_meta=True, tag=""):
+    log(f"[case] {tag} B={inp.batch} s_q={inp.s_q} h_q={inp.h_q} causal={inp.causal} "
+        f"lens={inp.seqlens.tolist()[:8]} parts={num_partitions}")
+    out, lse = run_decode(inp, num_partitions=num_partitions, use_meta=use_meta)
+    ref_out, ref_lse = oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table,
+                                             inp.seqlens, inp.scale, inp.causal, seqs=seqs)
+    sc = score(out, lse, ref_out, ref_lse, seqs=seqs)
+    log(f"       {sc}")
+    assert sc.ok(), f"{tag}: {sc}"
+    return out, lse
+
+
+SMALL_CASES = [
+    # (seqlens, s_q, h_q, causal)
+    ([37, 100], 1, 16, False),
+    ([1, 63, 64, 65, 127, 128, 129, 300], 1, 16, False),
+    ([0, 5, 0, 200], 1, 16, False),
+    ([700, 1], 1, 32, False),
+    ([130, 257, 64], 1, 64, False),
+    ([200, 333], 1, 128, False),
+    ([2, 3, 65, 190], 2, 128, True),
+    ([1, 70, 129], 2, 64, True),
+    ([90, 45], 1, 24, False),          # rows not a multiple of 16
+    ([150], 3, 8, True),               # M = 24, three causal tokens
+    ([1000, 17], 1, 16, True),         # causal with s_q = 1 is a no-op
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_small_shapes(case):
+    seqlens, s_q, h_q, causal = SMALL_CASES[case]
+    inp = make_inputs(seqlens, s_q, h_q, seed=100 + case, causal=causal)
+    _check(inp, tag=f"small[{case}]")
+
+
+@pytest.mark.parametrize("parts", [1, 8, 24, 64, 512])
+@pytest.mark.parametrize("shape", [(16, 1, False), (64, 1, False), (128, 2, True)])
+def test_forced_splits(parts, shape):
+    h_q, s_q, causal = shape
+    inp = make_inputs([900, 3, 2049, 64, 1500], s_q, h_q, seed=7 + parts, causal=causal)
+    _check(inp, num_partitions=parts, tag=f"splits h_q={h_q}")
+
+
+def test_metadata_computed_inside_decode():
+    inp = make_inputs([400, 90, 1200], 1, 16, seed=21)
+    a = run_decode(inp, num_partitions=64, use_meta=True)
+    b = run_decode(inp, num_partitions=64, use_meta=False)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_poisoned_tails_and_padding_are_ignored():
+    inp = make_inputs([37, 100, 129, 1], 2, 16, seed=22, causal=True, extra_blocks=3)
+    base = run_decode(inp, num_partitions=16)
+    bad = poison_block_table_padding(poison_page_tails(inp))
+    got = run_decode(bad, num_partitions=16)
+    assert np.array_equal(base[0], got[0]) and np.array_equal(base[1], got[1])
+
+
+def test_page_permutation_bitwise():
+    inp = make_inputs([513, 64, 1000], 1, 64, seed=23)
+    a = run_decode(inp, num_partitions=32)
+    b = run_decode(permute_pages(inp, 5), num_partitions=32)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_single_token_returns_value_row():
+    inp = make_inputs([1, 1, 1], 1, 16, seed=24)
+    out, lse = run_decode(inp)
+    for b in range(3):
+        row = inp.kv_bits[inp.block_table[b, 0], 0, 0, :512]
+        assert np.array_equal(out[b, 0], np.broadcast_to(row, (16, 512))), "out != V_0 bitwise"
+    _check(inp, tag="single token")
+
+
+def test_equal_scores_give_mean_of_values():
+    inp = make_inputs([300], 1, 16, seed=25)
+    inp.q_bits[...] = 0                                   # all scores 0
+    out, lse = run_decode(inp)
+    assert np.allclose(lse, np.log(300), atol=1e-3)
+    _check(inp, tag="equal scores")
+
+
+def test_empty_sequence_outputs_zero_and_neg_inf():
+    inp = make_inputs([0, 10, 0], 2, 16, seed=26, causal=True)
+    out, lse = run_decode(inp)
+    assert not np.any(out[0]) and not np.any(out[2])
+    assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[2]))
+    _check(inp, tag="empty")
+
+
+def test_device_metadata_matches_host():
+    import torch
+    import mla_paged_kv_02_amd as mla
+    rng = np.random.default_rng(27)
+    for h_q, s_q, parts in [(16, 1, 0), (64, 1, 256), (128, 2, 100), (16, 1, 3000)]:
+        seqlens = rng.integers(0, 9000, size=1500).astype(np.int32)
+        meta = mla.get_split_metadata(torch.from_numpy(seqlens).cuda(), h_q, s_q, parts)
+        host_parts = parts if parts > 0 else mla.default_num_partitions(h_q, s_q)
+        host = mla.split_metadata_host(seqlens, h_q, s_q, host_parts)
+        dev = meta.metadata.cpu().numpy()
+        assert np.array_equal(dev, host), f"device metadata differs for h_q={h_q} parts={parts}"
+
+
+def test_run_to_run_bitwise():
+    inp = make_inputs([3000, 77, 4097], 2, 128, seed=28, causal=True)
+    a = run_decode(inp)
+    b = run_decode(inp)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _sample_seqs(inp, k):
+    order = np.argsort(inp.seqlens)
+    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
+    rng = np.random.default_rng(0)
+    pick.update(int(x) for x in rng.choice(inp.batch, size=min(k, inp.batch), replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_named_workload_full_size(name):
+    inp = make_workload_inputs(name)
+    seqs = None if name == "tiny" else _sample_seqs(inp, 6)
+    _check(inp, seqs=seqs, tag=f"workload {name}")
