@@ -32,7 +32,8 @@ from workloads import (MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, algorithm
 METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
 DEFAULT_WORKLOAD = "memory_bound"
 KERNEL_SOURCES = ["mla_decode_kernel.hip", "mla_combine_kernel.hip", "mla_common.h", "mla_sched.h",
-                  "mla_api.cpp", "mla_internal.h", "mla_sched_kernel.hip"]
+                  "mla_api.cpp", "mla_internal.h", "mla_sched_kernel.hip", "mla_store_asm.h",
+                  "mla_decode_rows16.hip"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -182,6 +183,20 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     return line
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size, to calibrate the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) read by rocprofv3."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,11 +208,16 @@ def main():
                     help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
     ap.add_argument("--num-partitions", type=int, default=0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     for name in names:
         line = run_workload(name, args.steps, args.warmup,

@@ -70,9 +70,11 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.s_q = s_q;
     pl.M = (int)m;
     int tm = tile_rows_override();
-    if (tm == 0) tm = pl.M <= 16 ? 16 : pl.M <= 32 ? 32 : 64;
+    if (tm == 0) tm = pl.M <= 32 ? 16 : 64;
     pl.tm = tm;
-    // 4 waves of 16 query rows; waves sharing rows split the 512 value columns
+    // tm 16: four waves split the keys of one 16-row block (rows16 kernel);
+    // tm 32/64: four waves of 16 rows share each half page, waves sharing rows
+    // split the 512 value columns
     pl.nw = 4;
     pl.nc = 64 / tm;
     pl.R = (pl.M + tm - 1) / tm;

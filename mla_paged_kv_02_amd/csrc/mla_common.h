@@ -38,26 +38,53 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS accessors take generic pointers into __shared__ arrays and convert them
+// with address-space casts (not through integers), so the compiler can still
+// tell which LDS array an access touches.
+// One 16x16x16 BF16 product (K = 16), FP32 accumulate.
+__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                       __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 lds_read16(const uint8_t* p) {
-    return *reinterpret_cast<const MLA_AS3 bf16x8*>(
-        reinterpret_cast<const MLA_AS3 uint8_t*>(reinterpret_cast<uintptr_t>(p)));
+    return *(const MLA_AS3 bf16x8*)(p);
 }
 
 // Transposing LDS read: in each group of 16 lanes, lane i addresses row i/4,
 // elements 4*(i%4)..+3 of a 4 x 16 block of 16-bit values and receives column
 // i of that block (its 4 rows).
 __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(reinterpret_cast<MLA_AS3 bf16x4*>(
-        reinterpret_cast<MLA_AS3 uint8_t*>(reinterpret_cast<uintptr_t>(p))));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_AS3 bf16x4*)(p));
 }
 
 // 16-byte direct load from global memory into LDS. Every lane of the wave
 // supplies its own source; the wave's 64 chunks land contiguously at `lds_dst`
 // (lane k at byte 16*k), which must be the same for all lanes.
 __device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds(
-        reinterpret_cast<const MLA_AS1 void*>(reinterpret_cast<uintptr_t>(src)),
-        reinterpret_cast<MLA_AS3 void*>(reinterpret_cast<uintptr_t>(lds_dst)), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const MLA_AS1 void*)(src), (MLA_AS3 void*)(lds_dst), 16, 0, 0);
+}
+
+// Same transfer, issued so that the compiler does not track it: the caller
+// owns every wait for it (s_waitcnt vmcnt before reading the destination, and
+// before reusing it). `base` is wave-uniform, `voff` the lane's byte offset
+// from it, `lds_addr` the LDS byte address of lane 0's chunk. Used where the
+// compiler's own tracking of direct-to-LDS loads cannot tell two buffers
+// apart and would drain every load in flight before each LDS read.
+__device__ __forceinline__ void load_lds16_untracked(const void* base, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds_addr), "v"(voff), "s"(base)
+        : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(const MLA_AS3 void*)(p);
 }
 
 __device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
@@ -66,6 +93,12 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
     bf16x8 r;
     r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
     r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x4 pack_bf16x4(f32x4 v) {
+    bf16x4 r;
+    r[0] = (__bf16)v[0]; r[1] = (__bf16)v[1]; r[2] = (__bf16)v[2]; r[3] = (__bf16)v[3];
     return r;
 }
 
