@@ -61,8 +61,8 @@ def counter_traffic(workload: str):
 
 def cpu_baseline(workload: str, inp, budget_s: float):
     """The FP64 oracle, untuned, on a bounded sample of the same workload:
-    whole sequences in order until ~budget_s of CPU time. Reported in the
-    workload's algorithmic GB/s."""
+    whole sequences in order, wrapping round the batch, until ~budget_s of
+    wall time. Reported in the workload's algorithmic GB/s."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -72,7 +72,8 @@ def cpu_baseline(workload: str, inp, budget_s: float):
     w = WORKLOADS[workload]
     t0 = time.perf_counter()
     done = []
-    for b in range(inp.batch):
+    while True:
+        b = len(done) % inp.batch
         oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale,
                               inp.causal, seqs=[b])
         done.append(b)
@@ -80,10 +81,12 @@ def cpu_baseline(workload: str, inp, budget_s: float):
             break
     dt = time.perf_counter() - t0
     nbytes = algorithmic_bytes(inp.seqlens[done], w.s_q, w.h_q)
+    passes = len(done) / inp.batch
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {len(done)} of {inp.batch} sequences ({int(inp.seqlens[done].sum())} "
-                      f"tokens), {dt:.1f} s, numpy FP64 two-pass softmax per sequence"}
+            "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {inp.batch}-sequence "
+                      f"batch, {int(inp.seqlens[done].sum())} tokens) in {dt:.1f} s; numpy FP64 "
+                      f"two-pass softmax per sequence, GB/s from the same algorithmic-bytes formula"}
 
 
 def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_bytes: int,
@@ -119,36 +122,50 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    # (1) whole-step throughput: K steps between two events, nothing else
+    # recorded in between
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / steps
+    ms_step = t_start.elapsed_time(t_end) / steps
+    # (2) per-kernel durations: the library records HIP events on this stream
+    # around each decode and each combine kernel; torch events bracket each
+    # decode_fwd call. A separate pass, since the markers add dispatch gaps.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    mla.timing_enable(True)
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms_sum, comb_ms_sum, ncalls = mla.timing_collect()
+    mla.timing_enable(False)
+    assert ncalls == steps, f"timed {ncalls} calls, expected {steps}"
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     call_ms_mean = float(call_ms.mean())
+    dec_ms = dec_ms_sum / steps
+    comb_ms = comb_ms_sum / steps
 
     nbytes = algorithmic_bytes(inp.seqlens, w.s_q, w.h_q)
     flops = algorithmic_flops(inp.seqlens, w.s_q, w.h_q, w.causal)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
-    call_gbps = nbytes / (call_ms_mean * 1e-3) / 1e9
-    call_tflops = flops / (call_ms_mean * 1e-3) / 1e12
+    # roofline of the dominant kernel (the decode kernel): algorithmic bytes
+    # or FLOPs of one call over that kernel's mean event-timed duration
+    dec_gbps = nbytes / (dec_ms * 1e-3) / 1e9
+    dec_tflops = flops / (dec_ms * 1e-3) / 1e12
     hbm_bound = nbytes * 1.0 / (MI355X_HBM_GBPS * 1e9) >= flops * 1.0 / (MI355X_BF16_TFLOPS * 1e12)
     traffic = counter_traffic(name)
     if hbm_bound:
-        roof = {"bound": "hbm", "achieved": round(call_gbps, 1), "peak": MI355X_HBM_GBPS,
-                "unit": "GB/s", "frac": round(call_gbps / MI355X_HBM_GBPS, 4),
+        roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": MI355X_HBM_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / MI355X_HBM_GBPS, 4),
                 "traffic": traffic}
     else:
-        roof = {"bound": "mfma", "achieved": round(call_tflops, 2), "peak": MI355X_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(call_tflops / MI355X_BF16_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(dec_tflops, 2), "peak": MI355X_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dec_tflops / MI355X_BF16_TFLOPS, 4),
                 "traffic": traffic}
     line = {
         "metric": METRIC,
@@ -172,6 +189,8 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         "mfma_frac_of_peak": round(tflops / MI355X_BF16_TFLOPS, 4),
         "decode_call_us": round(call_ms_mean * 1e3, 2),
         "decode_call_us_min": round(float(call_ms.min()) * 1e3, 2),
+        "decode_kernel_us": round(dec_ms * 1e3, 2),
+        "combine_kernel_us": round(comb_ms * 1e3, 2),
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
         "kv_copies_rotated": copies,
@@ -197,6 +216,90 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def _counter_rows(run_dir: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {run_dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch_kib(run_dir: str, kernel_substr: str, counter: str):
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(run_dir)
+            if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernel '{kernel_substr}' in {run_dir}")
+    return float(np.mean(vals)), len(vals)
+
+
+def ingest_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
+                    cal_fetch_dir: str, cal_write_dir: str, command: str):
+    """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench on
+    `workload`, and of --copy-calibration) into HBM bytes per dispatch of
+    `kernel`, scaled so that the 1 GiB copy reads and writes 1 GiB, and store
+    them in profiles/hbm_traffic.json under the current kernel digest."""
+    cal_bytes = 1 << 30
+    cf, _ = _per_dispatch_kib(cal_fetch_dir, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _per_dispatch_kib(cal_write_dir, "copyBuffer", "WRITE_SIZE")
+    fetch_scale = cal_bytes / (cf * 1024.0)
+    write_scale = cal_bytes / (cw * 1024.0)
+    f, nf = _per_dispatch_kib(fetch_dir, kernel, "FETCH_SIZE")
+    wr, nw = _per_dispatch_kib(write_dir, kernel, "WRITE_SIZE")
+    entry = {
+        "kernel": kernel,
+        "kernel_digest": kernel_digest(),
+        "fetch_kib_per_dispatch": round(f, 1), "dispatches_fetch": nf,
+        "write_kib_per_dispatch": round(wr, 1), "dispatches_write": nw,
+        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        "copy_fetch_kib_per_gib": round(cf, 1), "copy_write_kib_per_gib": round(cw, 1),
+        "bytes_per_call": int(round(f * 1024.0 * fetch_scale + wr * 1024.0 * write_scale)),
+        "command": command,
+    }
+    try:
+        with open(COUNTERS_FILE) as fh:
+            doc = json.load(fh)
+    except (OSError, ValueError):
+        doc = {}
+    doc.setdefault("workloads", {})[workload] = entry
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(doc, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({workload: entry}))
+
+
+def summarize_trace(trace_dir: str, command: str, bench_log: str = "") -> str:
+    """Text summary of a rocprofv3 --kernel-trace --stats run (kernel stats CSV),
+    with the bench JSON line of the same run when its log is given."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    out = [f"command: {command}", f"kernel sources digest: {kernel_digest()}", "",
+           f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share':>7s}"]
+    for r in rows:
+        name = r["Name"].replace("(anonymous namespace)::", "")[:58]
+        out.append(f"{name:58s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                   f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                   f"{float(r['Percentage']):6.1f}%")
+    if bench_log:
+        for line in open(bench_log):
+            if line.startswith("{"):
+                d = json.loads(line)
+                out += ["", "bench.py line of the same run (under the profiler):",
+                        "  " + json.dumps({k: d[k] for k in ("decode_kernel_us", "combine_kernel_us",
+                                                              "decode_call_us", "ms_per_step",
+                                                              "roofline") if k in d})]
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,7 +313,22 @@ def main():
     ap.add_argument("--num-partitions", type=int, default=0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="rocprofv3 --pmc output dirs: write profiles/hbm_traffic.json for --workload "
+                         "(no GPU needed)")
+    ap.add_argument("--kernel", default="mla_decode_rows16_kernel",
+                    help="kernel name substring for --ingest-counters")
+    ap.add_argument("--command", default="", help="profiling command recorded by --ingest-counters")
+    ap.add_argument("--summarize-trace", nargs="+", metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="print a text summary of a rocprofv3 --kernel-trace --stats run (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace[0], args.command,
+                                         args.summarize_trace[1] if len(args.summarize_trace) > 1 else ""))
+        return
+    if args.ingest_counters:
+        ingest_counters(args.workload, args.kernel, *args.ingest_counters, command=args.command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
               file=sys.stderr)

@@ -161,6 +161,25 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
                           const int32_t* metadata, int num_partitions, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 
+/*
+ * Kernel timing for benchmarks (not part of the attention semantics).
+ *
+ * mla_timing_enable(1) makes every following mla_decode_fwd call on this
+ * process record HIP events on its own stream around its decode kernel and
+ * around its combine kernel; mla_timing_enable(0) stops recording and drops
+ * what was recorded. Events are created by the library on first use and
+ * reused; at most 4096 calls are recorded, later calls are not timed.
+ * Returns MLA_OK, or MLA_ERR_HIP if an event cannot be created.
+ *
+ * mla_timing_collect: once every recorded call has completed (the caller
+ * synchronises the streams first), writes the summed milliseconds of the
+ * decode kernels and of the combine kernels and the number of calls, then
+ * clears the record. Any output pointer may be NULL. Returns MLA_ERR_HIP if
+ * an event has not completed or cannot be read.
+ */
+mla_status mla_timing_enable(int enable);
+mla_status mla_timing_collect(double* decode_ms, double* combine_ms, int* calls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,3 +166,20 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
     check(status, "mla_decode_fwd")
     return out, lse
+
+
+def timing_enable(enable: bool = True) -> None:
+    """Record HIP events around the decode and combine kernels of every
+    following decode_fwd call (mla_timing_enable)."""
+    check(lib().mla_timing_enable(1 if enable else 0), "mla_timing_enable")
+
+
+def timing_collect() -> Tuple[float, float, int]:
+    """(decode kernel ms summed, combine kernel ms summed, calls) over the calls
+    recorded since the last collect; synchronise first (mla_timing_collect)."""
+    d = ctypes.c_double()
+    c = ctypes.c_double()
+    n = ctypes.c_int()
+    check(lib().mla_timing_collect(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)),
+          "mla_timing_collect")
+    return d.value, c.value, n.value

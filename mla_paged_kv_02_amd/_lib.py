@@ -30,6 +30,9 @@ SIGNATURES = {
     "mla_get_split_metadata_host": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size]),
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_timing_enable": (_c_int, [_c_int]),
+    "mla_timing_collect": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(_c_int)]),
 }
 
 MLA_OK = 0

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "mla_common.h"
 #include "mla_internal.h"
@@ -55,6 +56,38 @@ int tile_rows_override() {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Benchmark timing: three events per recorded call (before decode, between
+// decode and combine, after combine), pooled and reused.
+struct CallEvents {
+    hipEvent_t ev[3];
+};
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<CallEvents> pool;
+    size_t used = 0;
+};
+Timing g_timing;
+constexpr size_t kMaxTimedCalls = 4096;
+
+// Events for the next call, or nullptr when timing is off or full.
+CallEvents* timing_slot() {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (!g_timing.on || g_timing.used >= kMaxTimedCalls) return nullptr;
+    if (g_timing.used == g_timing.pool.size()) {
+        CallEvents ce{};
+        for (int i = 0; i < 3; ++i) {
+            if (hipEventCreate(&ce.ev[i]) != hipSuccess) {
+                (void)hipGetLastError();
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(ce.ev[j]);
+                return nullptr;
+            }
+        }
+        g_timing.pool.push_back(ce);
+    }
+    return &g_timing.pool[g_timing.used++];
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 }  // namespace
@@ -70,7 +103,7 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.s_q = s_q;
     pl.M = (int)m;
     int tm = tile_rows_override();
-    if (tm == 0) tm = pl.M <= 32 ? 16 : 64;
+    if (tm == 0) tm = pl.M <= 64 ? 16 : 64;
     pl.tm = tm;
     // tm 16: four waves split the keys of one 16-row block (rows16 kernel);
     // tm 32/64: four waves of 16 rows share each half page, waves sharing rows
@@ -248,8 +281,40 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     a.P = pl.P;
     a.scale_log2 = softmax_scale * kLog2e;
     a.causal = causal;
+    CallEvents* te = timing_slot();
+    if (te && hipEventRecord(te->ev[0], st) != hipSuccess) return MLA_ERR_HIP;
     if (launch_decode(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
+    if (te && hipEventRecord(te->ev[1], st) != hipSuccess) return MLA_ERR_HIP;
     if (launch_combine(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
+    if (te && hipEventRecord(te->ev[2], st) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+mla_status mla_timing_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.on = enable != 0;
+    g_timing.used = 0;
+    return MLA_OK;
+}
+
+mla_status mla_timing_collect(double* decode_ms, double* combine_ms, int* calls) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double d = 0.0, c = 0.0;
+    for (size_t i = 0; i < g_timing.used; ++i) {
+        float t0 = 0.f, t1 = 0.f;
+        const CallEvents& ce = g_timing.pool[i];
+        if (hipEventElapsedTime(&t0, ce.ev[0], ce.ev[1]) != hipSuccess ||
+            hipEventElapsedTime(&t1, ce.ev[1], ce.ev[2]) != hipSuccess) {
+            (void)hipGetLastError();
+            return MLA_ERR_HIP;
+        }
+        d += t0;
+        c += t1;
+    }
+    if (decode_ms) *decode_ms = d;
+    if (combine_ms) *combine_ms = c;
+    if (calls) *calls = (int)g_timing.used;
+    g_timing.used = 0;
     return MLA_OK;
 }
 

@@ -99,3 +99,13 @@ def test_host_metadata_rejects_negative_lengths():
     meta = np.zeros(4096, dtype=np.int32)
     st = _lib.lib().mla_get_split_metadata_host(sl.ctypes.data, 2, 16, 1, 8, meta.ctypes.data, meta.nbytes)
     assert st == INVALID
+
+
+def test_timing_record_is_empty_without_calls():
+    lib = _lib.lib()
+    d, c, n = ctypes.c_double(-1), ctypes.c_double(-1), ctypes.c_int(-1)
+    assert lib.mla_timing_enable(1) == OK
+    assert lib.mla_timing_collect(ctypes.byref(d), ctypes.byref(c), ctypes.byref(n)) == OK
+    assert (d.value, c.value, n.value) == (0.0, 0.0, 0)
+    assert lib.mla_timing_collect(None, None, None) == OK
+    assert lib.mla_timing_enable(0) == OK
