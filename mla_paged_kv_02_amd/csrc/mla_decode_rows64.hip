@@ -1,0 +1,344 @@
+// mla_decode_rows64.hip - split-KV MLA decode for blocks of 64 query rows.
+//
+// Method as in the other decode kernels (page "MLA 和 MHA 的 Kernel 区别",
+// section "MLA 的 FlashAttention": stream latent-cache tiles through on-chip
+// memory, score the query block against them, one-pass softmax; absorbed
+// form), organised for query blocks large enough that the two products are
+// the work: every page is brought into LDS once per workgroup and used by 64
+// query rows.
+//
+//  * four waves, wave w owns query rows 16w..16w+15 of the block (query in
+//    registers, O^T accumulators for its 16 rows x 512 columns in AGPRs);
+//  * the cache streams through a ring of four half-page slots (32 keys,
+//    36 KB each); wave w loads rows 8w..8w+7 of every half page with 16-byte
+//    direct loads, three half pages ahead of the one in use, and one
+//    workgroup barrier per half page makes the slot visible to all waves and
+//    frees the slot of the previous half page;
+//  * per half page a wave computes S^T = K Q^T for 32 keys (2 x 18 MFMA
+//    16x16x32) and O^T += V^T P^T with depth 32 (32 MFMA 16x16x32): a lane's
+//    eight softmax weights (4 keys of each 16-key tile) are exactly its B
+//    operand and the matching V^T operand is two transposing LDS reads;
+//  * softmax reference fixed per row at its first visible maximum plus a
+//    margin; if a later score would exceed it by more than the headroom, the
+//    wave raises a flag, every wave sees it after the next barrier and the
+//    workgroup redoes the segment with raised references (exact; never
+//    triggered by scores of realistic range);
+//  * no cross-wave merge: each wave finishes its own 16 rows.
+//
+// The direct-to-LDS loads are issued untracked by the compiler and every
+// wait for them is explicit.
+#include "mla_common.h"
+#include "mla_internal.h"
+#include "mla_sched.h"
+#include "mla_store_asm.h"
+
+namespace mla {
+
+namespace {
+
+__device__ __forceinline__ int ld_const_w(const int32_t* p, size_t i) {
+    return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+        reinterpret_cast<uintptr_t>(p))[i];
+}
+
+constexpr int kWaves = 4;
+constexpr int kCRows = 32;                      // keys per ring slot (half page)
+constexpr int kCBytes = kCRows * kRowBytes;     // 36864
+constexpr int kWLoads = 9;                      // a wave's wave-loads per slot (8 rows)
+constexpr int kKS = kHeadDim / 32;              // 18 k-steps of the score product
+constexpr int kNDT = kHeadDimV / 16;            // 32 output tiles of 16 columns
+constexpr float kRefMargin = 32.f;
+constexpr float kHeadroom = 64.f;
+
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+// a slot's loads are followed by two more slots' loads before it is read
+constexpr int kWaitSlot = wait_vm_lgkm0(2 * kWLoads);
+constexpr int kWaitAll = wait_vm_lgkm0(0);
+
+template <int kImm>
+__device__ __forceinline__ void wait_then_fence() {
+    __builtin_amdgcn_s_waitcnt(kImm);
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void mla_decode_rows64_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kCBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kCBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[kCBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[kCBytes];
+    // overflow flags by half-page parity: set during step c in flag[c & 1],
+    // read by every wave after the next barrier
+    __shared__ int restart_flag[2];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4;
+    const int i16 = lane & 15;
+
+    const int bid = blockIdx.x;
+    const int rb = (bid >> 3) % a.R;
+    const int p = ((bid >> 3) / a.R) * 8 + (bid & 7);
+
+    int b = ld_const_w(a.meta, kMetaHeader + 4 * p + 0);
+    int n = ld_const_w(a.meta, kMetaHeader + 4 * p + 1);
+    const int b_end = ld_const_w(a.meta, kMetaHeader + 4 * p + 2);
+    const int n_end = ld_const_w(a.meta, kMetaHeader + 4 * p + 3);
+    const int32_t* seqinfo = a.meta + kMetaHeader + 4 * a.P;
+
+    const int row = rb * 64 + wave * 16 + i16;
+    const bool row_ok = row < a.M;
+    const int tok = row_ok ? row / a.h_q : 0;
+
+    if (threadIdx.x == 0) {
+        restart_flag[0] = 0;
+        restart_flag[1] = 0;
+    }
+    const uint32_t slot_lds[4] = {lds_addr_of(ring0), lds_addr_of(ring1), lds_addr_of(ring2),
+                                  lds_addr_of(ring3)};
+
+    // Slot gather: wave w loads rows 8w..8w+7 of the half page with 9 wave
+    // loads of 1 KB; LDS 16-byte chunk k of the wave's 9 KB holds row k/72,
+    // slot k%72 = logical chunk slot^swz(row). The row (0..7) rides in the
+    // low bits of the 16-byte-aligned offset.
+    int goff[kWLoads];
+#pragma unroll
+    for (int j = 0; j < kWLoads; ++j) {
+        const int k = j * 64 + lane;
+        const int r = k / kRowChunks;
+        const int c = k - r * kRowChunks;
+        goff[j] = (r * kRowBytes + ((c ^ lds_swizzle(r)) << 4)) | r;
+    }
+    // Rows at or past the sequence end read the page's first kilobyte (row
+    // 0, always valid): finite data whose softmax weight is zero.
+    auto issue_half = [&](const uint8_t* page, int half, int valid, uint32_t dst) {
+        const int base = half * kCBytes + wave * 9216;
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j) {
+            const int off = goff[j];
+            const int r = half * kCRows + wave * 8 + (off & 7);
+            const uint32_t lo_off = r < valid ? (uint32_t)(base + (off & ~15)) : (uint32_t)(lane * 16);
+            load_lds16_untracked(page, lo_off, dst + wave * 9216 + j * 1024);
+        }
+    };
+
+    f32x4 o[kNDT];
+    bf16x8 qf[kKS];
+
+    while (b < b_end || (b == b_end && n < n_end)) {
+        const int nseq = ld_const_w(a.seqlens, b);
+        const int npages = pages_of(nseq);
+        const int hi = (b == b_end) ? n_end : npages;
+        if (n >= hi) { ++b; n = 0; continue; }
+        const int lo = n;
+        const int nch = 2 * (hi - lo);   // half pages of the segment
+
+        const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
+        auto page_of_chunk = [&](int c) {
+            const int pn = lo + (c < nch ? c : nch - 1) / 2;
+            return reinterpret_cast<const uint8_t*>(a.kv) +
+                   (size_t)ld_const_w(bt_row, pn) * kPageBytes;
+        };
+        // issue half page c (clamped to the last one) into its ring slot
+        auto issue_chunk = [&](int c, const uint8_t* page, uint32_t dst) {
+            const int cc = c < nch ? c : nch - 1;
+            issue_half(page, cc & 1, nseq - (lo + cc / 2) * kPageRows, dst);
+        };
+
+        const int L = a.causal ? min(max(nseq - a.s_q + tok + 1, 0), nseq) : nseq;
+        float m_ref = -INFINITY, l_run = 0.f;
+
+        // the wave's 16 query rows (rows past M repeat the block's first row;
+        // their results are never stored)
+        {
+            const uint16_t* qp = a.q + ((size_t)b * a.M + (row_ok ? row : rb * 64)) * kHeadDim + g * 8;
+#pragma unroll
+            for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+        }
+
+        bool restart = false;
+        do {
+            // fill slots 0..2, then drain: the query loads and the first
+            // three half pages are in, and every wave is past the previous
+            // use of the ring
+            issue_chunk(0, page_of_chunk(0), slot_lds[0]);
+            issue_chunk(1, page_of_chunk(1), slot_lds[1]);
+            issue_chunk(2, page_of_chunk(2), slot_lds[2]);
+            const uint8_t* page3 = page_of_chunk(3);
+            wait_then_fence<kWaitAll>();
+            block_barrier();
+            if (restart && wave == 0 && lane == 0) {
+                restart_flag[0] = 0;
+                restart_flag[1] = 0;
+            }
+#pragma unroll
+            for (int dt = 0; dt < kNDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            l_run = 0.f;
+            bool skip = false;   // this wave saw an overflow; PV is pointless until the restart
+
+            // One half page: chunk c sits in slot S = c % 4; chunk c+3 is
+            // issued into slot (S+3) % 4, whose previous chunk c-1 every
+            // wave finished before the barrier. Returns false when the
+            // segment is done or a restart is due.
+            int c = 0;
+            auto step = [&](auto sc) -> bool {
+                constexpr int S = decltype(sc)::value;
+                uint8_t* cur = S == 0 ? ring0 : S == 1 ? ring1 : S == 2 ? ring2 : ring3;
+                const uint8_t* page_next = page_of_chunk(c + 4);   // a step ahead
+                wait_then_fence<kWaitSlot>();
+                block_barrier();
+                if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
+                issue_chunk(c + 3, page3, slot_lds[(S + 3) % 4]);
+                page3 = page_next;
+
+                // ---- S^T = K Q^T for the slot's two 16-key tiles
+                f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                {
+                    constexpr int KD = 3;
+                    const int ksw = lds_swizzle(i16);
+                    const int koff = i16 * kRowBytes;
+                    auto k_off = [&](int ks) {
+                        const int ccx = ks * 4 + g;
+                        return koff + ((((ccx & 7) ^ ksw) << 4) | ((ccx >> 3) << 7));
+                    };
+                    bf16x8 k0[KD], k1[KD];
+#pragma unroll
+                    for (int d = 0; d < KD; ++d) {
+                        k0[d] = lds_read16(cur + k_off(d));
+                        k1[d] = lds_read16(cur + 16 * kRowBytes + k_off(d));
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < kKS; ++ks) {
+                        s0 = mfma16(k0[ks % KD], qf[ks], s0);
+                        s1 = mfma16(k1[ks % KD], qf[ks], s1);
+                        if (ks + KD < kKS) {
+                            k0[ks % KD] = lds_read16(cur + k_off(ks + KD));
+                            k1[ks % KD] = lds_read16(cur + 16 * kRowBytes + k_off(ks + KD));
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+
+                // ---- mask + reference check; lane holds row i16, keys
+                // 4g+j of tile 0 and 16+4g+j of tile 1
+                const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + 4 * g;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float v0 = (key0 + j < L) ? s0[j] * a.scale_log2 : -INFINITY;
+                    const float v1 = (key0 + 16 + j < L) ? s1[j] * a.scale_log2 : -INFINITY;
+                    s0[j] = v0;
+                    s1[j] = v1;
+                    mx = fmaxf(mx, fmaxf(v0, v1));
+                }
+                mx = fmaxf(mx, wave_xor(mx, 16));
+                mx = fmaxf(mx, wave_xor(mx, 32));
+                if (m_ref == -INFINITY) m_ref = mx == -INFINITY ? -INFINITY : mx + kRefMargin;
+                const bool over = mx > m_ref + kHeadroom;
+                if (__ballot(over) != 0) {
+                    if (over) m_ref = mx + kRefMargin;
+                    if (lane == 0) restart_flag[S & 1] = 1;
+                    skip = true;
+                }
+                if (!skip) {
+                    const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        s0[j] = __builtin_amdgcn_exp2f(s0[j] - m_use);
+                        s1[j] = __builtin_amdgcn_exp2f(s1[j] - m_use);
+                        l_run += s0[j] + s1[j];
+                    }
+                    // B = P^T: k-slot j <-> key 4g+j, k-slot 4+j <-> key 16+4g+j
+                    const bf16x8 pf = cat_bf16x4(pack_bf16x4(s0), pack_bf16x4(s1));
+
+                    // ---- O^T += V^T P^T, depth 32: A = V^T for keys
+                    // 4g..4g+3 and 16+4g..16+4g+3, two transposing reads
+                    constexpr int VD = 4;
+                    const int vr = 4 * g + (i16 >> 2);
+                    const int vsw = lds_swizzle(vr);
+                    const int vbase = vr * kRowBytes + ((i16 & 1) << 3);
+                    auto v_off = [&](int dt) {
+                        const int ccx = dt * 2 + ((i16 & 3) >> 1);
+                        return vbase + ((((ccx & 7) ^ vsw) << 4) | ((ccx >> 3) << 7));
+                    };
+                    auto v_frag = [&](int dt) {
+                        return cat_bf16x4(lds_read_tr(cur + v_off(dt)),
+                                          lds_read_tr(cur + 16 * kRowBytes + v_off(dt)));
+                    };
+                    bf16x8 vf[VD];
+#pragma unroll
+                    for (int d = 0; d < VD; ++d) vf[d] = v_frag(d);
+#pragma unroll
+                    for (int dt = 0; dt < kNDT; ++dt) {
+                        o[dt] = mfma16(vf[dt % VD], pf, o[dt]);
+                        if (dt + VD < kNDT) vf[dt % VD] = v_frag(dt + VD);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                ++c;
+                return c < nch;
+            };
+            using S0 = std::integral_constant<int, 0>;
+            using S1 = std::integral_constant<int, 1>;
+            using S2 = std::integral_constant<int, 2>;
+            using S3 = std::integral_constant<int, 3>;
+            while (step(S0{}) && step(S1{}) && step(S2{}) && step(S3{})) {
+            }
+            // drain the half pages still in flight; after the barrier every
+            // wave sees an overflow raised in the last half page too
+            wait_then_fence<kWaitAll>();
+            block_barrier();
+            restart = (restart_flag[0] | restart_flag[1]) != 0;
+            if (restart) block_barrier();   // every wave has read the flag before it is cleared
+        } while (restart);
+
+        // ---- epilogue: this wave's 16 rows
+        float lsum = l_run;
+        lsum += wave_xor(lsum, 16);
+        lsum += wave_xor(lsum, 32);
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        const float lse_v = lsum > 0.f ? (m_ref + __log2f(lsum)) * kLn2 : -INFINITY;
+        const bool full = (lo == 0) && (hi == npages);
+        if (row_ok) {
+            const int col0 = 4 * g;   // tile dt covers columns col0 + 16 dt .. +3
+            if (full) {
+                uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + col0;
+                bf16x4 v[kNDT];
+#pragma unroll
+                for (int dt = 0; dt < kNDT; ++dt) {
+                    f32x4 t = o[dt];
+                    t[0] *= inv; t[1] *= inv; t[2] *= inv; t[3] *= inv;
+                    v[dt] = pack_bf16x4(t);
+                }
+                TileStores<kNDT>::out(op, v);
+                if (g == 0) a.lse[(size_t)b * a.M + row] = lse_v;
+            } else {
+                const int slotno = ld_const_w(seqinfo, 4 * b + 0) + (p - ld_const_w(seqinfo, 4 * b + 1));
+                float* pp = a.part_o + ((size_t)slotno * a.M + row) * kHeadDimV + col0;
+                f32x4 v[kNDT];
+#pragma unroll
+                for (int dt = 0; dt < kNDT; ++dt) {
+                    v[dt] = o[dt];
+                    v[dt][0] *= inv; v[dt][1] *= inv; v[dt][2] *= inv; v[dt][3] *= inv;
+                }
+                TileStores<kNDT>::part(pp, v);
+                if (g == 0) a.part_lse[(size_t)slotno * a.M + row] = lse_v;
+            }
+        }
+        ++b;
+        n = 0;
+    }
+}
+
+hipError_t launch_decode_rows64(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_decode_rows64_kernel, dim3(plan.P * plan.R), dim3(256), 0, stream, args);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -54,6 +54,7 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
                                  int32_t* meta, hipStream_t stream);
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_rows64(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 
 // Host build of the same plan (tests and host callers).
