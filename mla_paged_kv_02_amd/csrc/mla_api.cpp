@@ -106,7 +106,7 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     if (tm == 0) tm = pl.M <= 64 ? 16 : 64;
     pl.tm = tm;
     // tm 16: four waves split the keys of one 16-row block (rows16 kernel);
-    // tm 64: four waves of 16 rows share each half page (rows64 kernel);
+    // tm 64: four waves of 16 rows share each half page (wide kernel);
     // tm 32: two waves per 16 rows split the value columns (multi-row kernel)
     pl.nw = 4;
     pl.nc = tm == 32 ? 2 : 0;

@@ -89,6 +89,23 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
 
 __device__ __forceinline__ float wave_xor(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum over the four lanes i, i^16, i^32, i^48 (the k-groups of one
+// MFMA column) with the lane-swap VALU ops, which stay out of the LDS queue.
+// permlane16_swap(x, x) leaves x[l & ~16] and x[l | 16] in its two results,
+// permlane32_swap(x, x) leaves x[l & ~32] and x[l | 32].
+__device__ __forceinline__ float max_over_kgroups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_kgroups(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
     bf16x8 r;
     r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];

@@ -109,31 +109,54 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
 
     // Stripe gather: 18 wave loads of 1 KB; LDS 16-byte chunk k holds stripe
     // row k/72, slot k%72 = logical chunk slot^swz(row). Nine loads cover
-    // eight rows, so the lane's nine (row, offset) pairs repeat; the row
-    // (0..7) rides in the low bits of the 16-byte-aligned offset.
+    // eight rows, so the lane's nine source offsets repeat for rows 8..15.
     int goff[9];
 #pragma unroll
     for (int j = 0; j < 9; ++j) {
         const int k = j * 64 + lane;
         const int r = k / kRowChunks;
         const int c = k - r * kRowChunks;
-        goff[j] = (r * kRowBytes + ((c ^ lds_swizzle(r)) << 4)) | r;
+        goff[j] = r * kRowBytes + ((c ^ lds_swizzle(r)) << 4);
     }
     // Rows at or past the sequence end read the page's first kilobyte (row 0,
-    // always valid): finite data whose softmax weight is zero.
+    // always valid): finite data whose softmax weight is zero. Only the last
+    // page of a sequence takes that path.
     auto issue_stripe = [&](const uint8_t* page, int valid, uint32_t dst) {
+        if (valid >= kSRows) {
+            const uint8_t* src = page + wave * kSBytes;
 #pragma unroll
-        for (int grp = 0; grp < 2; ++grp) {
+            for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-            for (int j = 0; j < 9; ++j) {
-                const int off = goff[j];
-                const int r = grp * 8 + (off & 7);
-                const uint32_t lo_off = r < valid ? (uint32_t)(wave * kSBytes + grp * 9216 + (off & ~15))
-                                                 : (uint32_t)(lane * 16);
-                load_lds16_untracked(page, lo_off, dst + grp * 9216 + j * 1024);
+                for (int j = 0; j < 9; ++j)
+                    load_lds16_untracked(src, (uint32_t)(grp * 9216 + goff[j]), dst + grp * 9216 + j * 1024);
+        } else {
+#pragma unroll
+            for (int grp = 0; grp < 2; ++grp) {
+#pragma unroll
+                for (int j = 0; j < 9; ++j) {
+                    const int r = grp * 8 + (j * 64 + lane) / kRowChunks;
+                    const uint32_t lo_off = r < valid ? (uint32_t)(wave * kSBytes + grp * 9216 + goff[j])
+                                                     : (uint32_t)(lane * 16);
+                    load_lds16_untracked(page, lo_off, dst + grp * 9216 + j * 1024);
+                }
             }
         }
     };
+
+    // LDS byte offsets inside a stripe, precomputed per lane: the K fragment
+    // of k-step ks for key row i16 is at kofs[ks & 1] + 128 (ks >> 1); the
+    // V^T fragment of value tile dt for key rows vr = 4g + i16/4 at
+    // vofs[dt & 3] + 128 (dt >> 2).
+    int kofs[2], vofs[4];
+    {
+        const int vr = 4 * g + (i16 >> 2);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            kofs[i] = i16 * kRowBytes + (((i * 4 + g) ^ lds_swizzle(i16)) << 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            vofs[i] = vr * kRowBytes + ((i16 & 1) << 3) + (((i * 2 + ((i16 & 3) >> 1)) ^ lds_swizzle(vr)) << 4);
+    }
 
     f32x4 o[kNDT];
     const uint8_t* const q_frag = qlds + lane * 16;
@@ -198,12 +221,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             {
                 constexpr int KD = 4;
-                const int koff = i16 * kRowBytes;
-                const int ksw = lds_swizzle(i16);
-                auto k_off = [&](int ks) {
-                    const int cc = ks * 4 + g;
-                    return koff + ((((cc & 7) ^ ksw) << 4) | ((cc >> 3) << 7));
-                };
+                auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
                 bf16x8 kf[KD], qf[KD];
 #pragma unroll
                 for (int d = 0; d < KD; ++d) {
@@ -230,8 +248,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
                 s[j] = v;
                 mx = fmaxf(mx, v);
             }
-            mx = fmaxf(mx, wave_xor(mx, 16));
-            mx = fmaxf(mx, wave_xor(mx, 32));
+            mx = max_over_kgroups(mx);
             // A row with no visible key so far has O = 0 and l = 0, so its
             // reference can be set freely.
             if (m_ref == -INFINITY) m_ref = mx == -INFINITY ? -INFINITY : mx + kRefMargin;
@@ -256,13 +273,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
             // transposing read.
             {
                 constexpr int VD = 8;
-                const int vr = 4 * g + (i16 >> 2);
-                const int vsw = lds_swizzle(vr);
-                const int vbase = vr * kRowBytes + ((i16 & 1) << 3);
-                auto v_off = [&](int dt) {
-                    const int cc = dt * 2 + ((i16 & 3) >> 1);
-                    return vbase + ((((cc & 7) ^ vsw) << 4) | ((cc >> 3) << 7));
-                };
+                auto v_off = [&](int dt) { return vofs[dt & 3] + (dt >> 2) * 128; };
                 bf16x4 vf[VD];
 #pragma unroll
                 for (int d = 0; d < VD; ++d) vf[d] = lds_read_tr(cur + v_off(d));
@@ -307,8 +318,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
         // follow the tiles in buf0. Only this wave has touched its entries
         // since the last barrier, so no barrier is needed before writing.
         float lsum = l_run;
-        lsum += wave_xor(lsum, 16);
-        lsum += wave_xor(lsum, 32);
+        lsum = sum_over_kgroups(lsum);
         {
             float* w0 = reinterpret_cast<float*>(mine0);
             float* w1 = reinterpret_cast<float*>(mine1);
