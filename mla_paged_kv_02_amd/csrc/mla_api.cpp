@@ -43,13 +43,16 @@ int current_cu_count() {
     return g_cu_count[dev];
 }
 
-// Optional override of the rows per workgroup (16, 32 or 64), read once.
-int tile_rows_override() {
+// Optional override of the kernel choice, read once: -1 when unset.
+int kernel_override() {
     static int v = []() {
-        const char* e = std::getenv("MLA_TILE_ROWS");
-        if (!e) return 0;
-        int t = std::atoi(e);
-        return (t == 16 || t == 32 || t == 64) ? t : 0;
+        const char* e = std::getenv("MLA_DECODE_KERNEL");
+        if (!e) return -1;
+        if (!std::strcmp(e, "rows16")) return static_cast<int>(DecodeKernel::Rows16);
+        if (!std::strcmp(e, "wide")) return static_cast<int>(DecodeKernel::Wide);
+        if (!std::strcmp(e, "ws")) return static_cast<int>(DecodeKernel::WaveSplit);
+        if (!std::strcmp(e, "ring")) return static_cast<int>(DecodeKernel::Ring);
+        return -1;
     }();
     return v;
 }
@@ -102,14 +105,25 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.h_q = h_q;
     pl.s_q = s_q;
     pl.M = (int)m;
-    int tm = tile_rows_override();
-    if (tm == 0) tm = pl.M <= 64 ? 16 : 64;
+    // Kernel choice (MLA_DECODE_KERNEL=rows16|wide|ws|ring overrides it):
+    //   rows16: four waves split the keys of one 16-row block (M <= 64);
+    //   ws:     64-row blocks, four score waves and four value waves (M > 64);
+    //   wide:   64-row blocks, four waves of 16 rows doing both products;
+    //   ring:   32-row blocks, multi-row kernel with split value columns.
+    DecodeKernel k = pl.M <= 64 ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
+    const int ov = kernel_override();
+    if (ov >= 0) k = static_cast<DecodeKernel>(ov);
+    int tm = 16;
+    switch (k) {
+        case DecodeKernel::Rows16: tm = 16; break;
+        case DecodeKernel::Wide: tm = 64; break;
+        case DecodeKernel::WaveSplit: tm = 64; break;
+        case DecodeKernel::Ring: tm = 32; break;
+    }
+    pl.kernel = k;
     pl.tm = tm;
-    // tm 16: four waves split the keys of one 16-row block (rows16 kernel);
-    // tm 64: four waves of 16 rows share each half page (wide kernel);
-    // tm 32: two waves per 16 rows split the value columns (multi-row kernel)
     pl.nw = 4;
-    pl.nc = tm == 32 ? 2 : 0;
+    pl.nc = k == DecodeKernel::Ring ? 2 : 0;
     pl.R = (pl.M + tm - 1) / tm;
     int p = num_partitions;
     if (p <= 0) {

@@ -393,17 +393,17 @@ __global__ __launch_bounds__(NW * 64) void mla_decode_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
-    const dim3 grid(plan.P * plan.R);
-    if (plan.tm == 16) return launch_decode_rows16(plan, args, stream);
-    if ((plan.tm == 64 || plan.tm == 128) && plan.nc == 0) return launch_decode_rows64(plan, args, stream);
-    if (plan.nw == 4 && plan.nc == 2) {
-        hipLaunchKernelGGL((mla_decode_kernel<4, 2>), grid, dim3(256), 0, stream, args);
-    } else if (plan.nw == 4 && plan.nc == 1) {
-        hipLaunchKernelGGL((mla_decode_kernel<4, 1>), grid, dim3(256), 0, stream, args);
-    } else {
-        return hipErrorInvalidValue;
+    switch (plan.kernel) {
+        case DecodeKernel::Rows16: return launch_decode_rows16(plan, args, stream);
+        case DecodeKernel::Wide: return launch_decode_rows64(plan, args, stream);
+        case DecodeKernel::WaveSplit: return launch_decode_ws(plan, args, stream);
+        case DecodeKernel::Ring: break;
     }
-    return hipGetLastError();
+    if (plan.nw == 4 && plan.nc == 2) {
+        hipLaunchKernelGGL((mla_decode_kernel<4, 2>), dim3(plan.P * plan.R), dim3(256), 0, stream, args);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mla

@@ -12,8 +12,11 @@ namespace mla {
 //   every wave owns 16 query rows and 512/nc value columns
 //   R row blocks cover the M = h_q*s_q rows of a sequence; P partitions cut
 //   the page list; the grid is P*R workgroups.
+enum class DecodeKernel { Rows16, Wide, WaveSplit, Ring };
+
 struct Plan {
     int batch, h_q, s_q, M;
+    DecodeKernel kernel;
     int tm, nw, nc;
     int R, P;
     int cseg;
@@ -55,6 +58,7 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows64(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 
 // Host build of the same plan (tests and host callers).
