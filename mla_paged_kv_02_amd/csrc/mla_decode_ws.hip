@@ -16,10 +16,12 @@
 //    tiles instead of one. While a score wave waits on LDS or runs its exps,
 //    the value wave on the same SIMD keeps the matrix core busy;
 //  * the cache streams through a ring of four half-page slots (32 keys,
-//    36 KB): the score waves load them with 16-byte direct loads, two half
-//    pages ahead; one workgroup barrier per step publishes a slot, the
-//    weights of the previous half page and frees the slot the value waves
-//    finished. Step c scores half page c and accumulates half page c-1;
+//    36 KB): the value waves load them with 16-byte direct loads, two half
+//    pages ahead, while the score waves compute scores; a workgroup barrier
+//    starts each step (publishing a slot and the previous weights, freeing
+//    the slot the value waves finished) and one splits it in halves, so
+//    that 16-byte K reads and transposing V reads never share the LDS. Step
+//    c scores half page c and accumulates half page c-1;
 //  * softmax reference fixed per row at its first visible maximum plus a
 //    margin; a score beyond the headroom raises a flag that every wave reads
 //    after the next barrier, and the workgroup redoes the segment with raised
@@ -46,7 +48,7 @@ __device__ __forceinline__ int ld_const_ws(const int32_t* p, size_t i) {
 constexpr int kScoreWaves = 4;
 constexpr int kCRows = 32;                      // keys per ring slot (half page)
 constexpr int kCBytes = kCRows * kRowBytes;     // 36864
-constexpr int kWLoads = 9;                      // a score wave's wave-loads per slot (8 rows)
+constexpr int kWLoads = 9;                      // a value wave's wave-loads per slot (8 rows)
 constexpr int kKS = kHeadDim / 32;              // 18 k-steps of the score product
 constexpr int kVTiles = 8;                      // value tiles (16 columns) per value wave
 constexpr float kRefMargin = 32.f;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     const uint32_t slot_lds[4] = {lds_addr_of(ring0), lds_addr_of(ring1), lds_addr_of(ring2),
                                   lds_addr_of(ring3)};
 
-    // score wave s gathers rows 8s..8s+7 of every half page: LDS 16-byte
+    // value wave v gathers rows 8v..8v+7 of every half page: LDS 16-byte
     // chunk k of its 9 KB holds row k/72, slot k%72 = logical chunk
     // slot^swz(row); goff[j] is the lane's source offset for load j
     int goff[kWLoads];
@@ -194,19 +196,20 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 
             bool restart = false;
             do {
+                // value waves fill slots 0 and 1; the score waves' query
+                // loads are the compiler's own and waited for where used
                 const uint8_t* page2 = nullptr;
-                if constexpr (kScorer) {
+                if constexpr (!kScorer) {
                     issue_chunk(0, page_of_chunk(0), slot_lds[0]);
                     issue_chunk(1, page_of_chunk(1), slot_lds[1]);
                     page2 = page_of_chunk(2);
-                    // the query and the first two half pages are in
                     wait_then_fence<kWaitAll>();
-                    l_run = 0.f;
-                } else {
 #pragma unroll
                     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                         for (int t = 0; t < kVTiles; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else {
+                    l_run = 0.f;
                 }
                 block_barrier();   // every wave is past the previous use of the ring
                 if (restart && wid == 0 && lane == 0) {
@@ -215,57 +218,71 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
                 bool skip = false;   // overflow seen: no more weights until the restart
 
-                // Step c: score half page c (c < nch), accumulate half page
-                // c-1 (c >= 1). Slot S = c % 4 is scored, slot (S+3) % 4
-                // accumulated, slot (S+2) % 4 refilled with half page c+2 (its
-                // previous contents, half page c-2, were accumulated in step c-1).
+                // Step c, first half: the value waves issue half page c+2
+                // into slot (S+2) % 4 (its previous contents, half page c-2,
+                // were accumulated in step c-1) while the score waves compute
+                // S^T for half page c from slot S = c % 4. Second half: the
+                // score waves turn the scores into weights while the value
+                // waves accumulate half page c-1 from slot (S+3) % 4. The
+                // 16-byte K reads and the transposing V reads stay in
+                // separate halves: concurrent transposing reads starve the
+                // others in the LDS.
                 int c = 0;
                 auto step = [&](auto sc) -> bool {
                     constexpr int S = decltype(sc)::value;
                     const uint8_t* page_next = nullptr;
-                    if constexpr (kScorer) {
+                    if constexpr (!kScorer) {
                         wait_then_fence<kWaitSlot>();   // my part of half page c
                         page_next = page_of_chunk(c + 3);
+                    } else {
+                        // weights and flags of step c-1 are written
+                        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
+                        asm volatile("" ::: "memory");
                     }
                     block_barrier();
-                    if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
-                    if constexpr (kScorer) {
+                    const int flag = restart_flag[(S + 1) & 1];   // raised in step c-1; acted on below
+                    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                    if constexpr (!kScorer) {
                         issue_chunk(c + 2, page2, slot_lds[(S + 2) % 4]);
                         page2 = page_next;
+                    } else if (c < nch) {
+                        const uint8_t* cur = slots[S];
+                        // ---- S^T = K Q^T, key tiles 0 and 1, two chains each
+                        f32x4 sp[2][2];
+#pragma unroll
+                        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                            for (int pp = 0; pp < 2; ++pp) sp[kt][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        constexpr int KD = 4;
+                        auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
+                        bf16x8 k0[KD], k1[KD];
+#pragma unroll
+                        for (int d = 0; d < KD; ++d) {
+                            k0[d] = lds_read16(cur + k_off(d));
+                            k1[d] = lds_read16(cur + 16 * kRowBytes + k_off(d));
+                        }
+#pragma unroll
+                        for (int ks = 0; ks < kKS; ++ks) {
+                            sp[0][ks & 1] = mfma16(k0[ks % KD], qf[ks], sp[0][ks & 1]);
+                            sp[1][ks & 1] = mfma16(k1[ks % KD], qf[ks], sp[1][ks & 1]);
+                            if (ks + KD < kKS) {
+                                k0[ks % KD] = lds_read16(cur + k_off(ks + KD));
+                                k1[ks % KD] = lds_read16(cur + 16 * kRowBytes + k_off(ks + KD));
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        s0 = sp[0][0];
+                        s1 = sp[1][0];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            s0[j] += sp[0][1][j];
+                            s1[j] += sp[1][1][j];
+                        }
+                    }
+                    block_barrier();   // the K reads of this step are done
+                    if (flag != 0) return false;
+                    if constexpr (kScorer) {
                         if (c < nch) {
-                            const uint8_t* cur = slots[S];
-                            // ---- S^T = K Q^T, key tiles 0 and 1, two chains each
-                            f32x4 sp[2][2];
-#pragma unroll
-                            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                                for (int pp = 0; pp < 2; ++pp) sp[kt][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-                            {
-                                constexpr int KD = 4;
-                                auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
-                                bf16x8 k0[KD], k1[KD];
-#pragma unroll
-                                for (int d = 0; d < KD; ++d) {
-                                    k0[d] = lds_read16(cur + k_off(d));
-                                    k1[d] = lds_read16(cur + 16 * kRowBytes + k_off(d));
-                                }
-#pragma unroll
-                                for (int ks = 0; ks < kKS; ++ks) {
-                                    sp[0][ks & 1] = mfma16(k0[ks % KD], qf[ks], sp[0][ks & 1]);
-                                    sp[1][ks & 1] = mfma16(k1[ks % KD], qf[ks], sp[1][ks & 1]);
-                                    if (ks + KD < kKS) {
-                                        k0[ks % KD] = lds_read16(cur + k_off(ks + KD));
-                                        k1[ks % KD] = lds_read16(cur + 16 * kRowBytes + k_off(ks + KD));
-                                    }
-                                    __builtin_amdgcn_sched_barrier(0);
-                                }
-                            }
-                            f32x4 s0 = sp[0][0], s1 = sp[1][0];
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                s0[j] += sp[0][1][j];
-                                s1[j] += sp[1][1][j];
-                            }
                             // ---- mask + reference check; lane holds keys
                             // 4g+j of key tile 0 and 16+4g+j of key tile 1
                             const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + 4 * g;
@@ -307,7 +324,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                         bf16x8 pf[4];
 #pragma unroll
                         for (int rt = 0; rt < 4; ++rt) pf[rt] = lds_read16(pb + rt * 1024);
-                        constexpr int VD = 3;
+                        constexpr int VD = 5;
                         auto v_frag = [&](int t) {
                             const int dt = sw * kVTiles + t;
                             const int off = vofs[dt & 3] + (dt >> 2) * 128;
@@ -335,7 +352,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
                 // drain the half pages still in flight; after the barrier
                 // every wave sees an overflow raised in the last step too
-                if constexpr (kScorer) wait_then_fence<kWaitAll>();
+                wait_then_fence<kWaitAll>();
                 block_barrier();
                 restart = (restart_flag[0] | restart_flag[1]) != 0;
                 if (restart) block_barrier();   // every wave has read the flag before it is cleared
