@@ -8,6 +8,13 @@
 // sets). Splitting the key range this way is what lets decode with a small
 // batch use the whole GPU (long-text inference page, "Unlocking GPU
 // Potential ...").
+//
+// The work is pure streaming of FP32 partial rows (2 KB per row and
+// partial). An item is one half row (256 columns, 16 bytes per lane) of one
+// sequence. With few partials per sequence a block of four waves takes four
+// items, one wave each; with many (long sequences on a small batch) the 4 or
+// 16 waves of a block share one item's partials and sum them through LDS, so
+// that each wave has only a round trip or two of loads to wait for.
 #include "mla_common.h"
 #include "mla_internal.h"
 #include "mla_sched.h"
@@ -16,27 +23,62 @@ namespace mla {
 
 namespace {
 
-constexpr int kCombineRows = 4;  // one wave per row
+constexpr int kCombineUnroll = 8;   // partial rows in flight per wave
 
-__global__ __launch_bounds__(64 * kCombineRows) void mla_combine_kernel(DecodeArgs a) {
+__device__ __forceinline__ float ld_const_f32(const float* p, size_t i) {
+    return reinterpret_cast<const __attribute__((address_space(4))) float*>(
+        reinterpret_cast<uintptr_t>(p))[i];
+}
+
+template <int kWPI>   // waves per item
+__global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel(DecodeArgs a) {
+    constexpr int kWaves = kWPI > 4 ? kWPI : 4;
+    constexpr int kItems = kWaves / kWPI;
+    __shared__ f32x4 red[kWPI > 1 ? kWaves : 1][64];
     const int b = blockIdx.x;
     const int lane = threadIdx.x & 63;
-    const int row = blockIdx.y * kCombineRows + (threadIdx.x >> 6);
-    if (row >= a.M) return;
-    const int32_t* si = a.meta + kMetaHeader + 4 * a.P + 4 * b;
-    const int cnt = si[2];
-    uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + lane * 8;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int item = blockIdx.y * kItems + w / kWPI;   // row * 2 + half
+    const int sub = w % kWPI;
+    const int row = item >> 1;
+    const int half = item & 1;
+    const bool live = row < a.M;
 
-    if (cnt <= 1) {
-        if (cnt == 0) {  // no pages: empty sequence
-            *reinterpret_cast<uint4*>(op) = uint4{0u, 0u, 0u, 0u};
-            if (lane == 0) a.lse[(size_t)b * a.M + row] = -INFINITY;
+    // sequence record {slot base, first partition, partition count, cost start}
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 si = reinterpret_cast<const __attribute__((address_space(4))) i32x4*>(
+        reinterpret_cast<uintptr_t>(a.meta + kMetaHeader + 4 * a.P))[b];
+    const int cnt = si.z;
+    if (cnt == 1) return;   // the decode kernel wrote this sequence's result
+    const int col = half * 256 + lane * 4;
+    uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + col;
+    if (cnt == 0) {   // no pages: empty sequence
+        if (live && sub == 0) {
+            *reinterpret_cast<uint2*>(op) = uint2{0u, 0u};
+            if (half == 0 && lane == 0) a.lse[(size_t)b * a.M + row] = -INFINITY;
         }
         return;
     }
-    const int base = si[0];
-    const float* lp = a.part_lse + (size_t)base * a.M + row;
+    const int base = si.x;
+    const int rr = live ? row : 0;
+    const float* lp = a.part_lse + (size_t)base * a.M + rr;
 
+    const float* pbase = a.part_o + ((size_t)base * a.M + rr) * kHeadDimV + col;
+    const size_t pstride = (size_t)a.M * kHeadDimV;
+    // this wave's partials are s = sub, sub + kWPI, ...; the first group is
+    // loaded before the lse reduction so that the two latencies overlap
+    f32x4 x[kCombineUnroll];
+    float wt[kCombineUnroll];
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+        const int su = sub + u * kWPI;
+        if (su < cnt) {
+            x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)su * pstride);
+            wt[u] = ld_const_f32(lp, (size_t)su * a.M);
+        }
+    }
+
+    // combined lse (every wave of the item computes it; a few loads per lane)
     float m = -INFINITY;
     for (int s = lane; s < cnt; s += 64) m = fmaxf(m, lp[(size_t)s * a.M]);
 #pragma unroll
@@ -48,27 +90,57 @@ __global__ __launch_bounds__(64 * kCombineRows) void mla_combine_kernel(DecodeAr
     for (int d = 1; d < 64; d <<= 1) tot += wave_xor(tot, d);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < cnt; ++s) {
-        const float w = __builtin_amdgcn_exp2f((lp[(size_t)s * a.M] - m_use) * kLog2e) * inv;
-        const float* pp = a.part_o + ((size_t)(base + s) * a.M + row) * kHeadDimV + lane * 8;
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(pp);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(pp + 4);
-        acc[0] += w * x0[0]; acc[1] += w * x0[1]; acc[2] += w * x0[2]; acc[3] += w * x0[3];
-        acc[4] += w * x1[0]; acc[5] += w * x1[1]; acc[6] += w * x1[2]; acc[7] += w * x1[3];
-    }
-    bf16x8 v;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto accumulate = [&](const f32x4& xv, float lse_s) {
+        const float wu = __builtin_amdgcn_exp2f((lse_s - m_use) * kLog2e);
+        acc[0] += wu * xv[0]; acc[1] += wu * xv[1]; acc[2] += wu * xv[2]; acc[3] += wu * xv[3];
+    };
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = (__bf16)acc[k];
-    *reinterpret_cast<bf16x8*>(op) = v;
-    if (lane == 0) a.lse[(size_t)b * a.M + row] = tot > 0.f ? (m_use + __log2f(tot) * kLn2) : -INFINITY;
+    for (int u = 0; u < kCombineUnroll; ++u)
+        if (sub + u * kWPI < cnt) accumulate(x[u], wt[u]);
+    int s = sub + kCombineUnroll * kWPI;
+    for (; s + (kCombineUnroll - 1) * kWPI < cnt; s += kCombineUnroll * kWPI) {
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)(s + u * kWPI) * pstride);
+            wt[u] = ld_const_f32(lp, (size_t)(s + u * kWPI) * a.M);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) accumulate(x[u], wt[u]);
+    }
+    for (; s < cnt; s += kWPI) accumulate(*reinterpret_cast<const f32x4*>(pbase + (size_t)s * pstride),
+                                          ld_const_f32(lp, (size_t)s * a.M));
+    if constexpr (kWPI > 1) {
+        red[w][lane] = acc;
+        __syncthreads();
+        if (sub != 0) return;
+#pragma unroll
+        for (int k = 1; k < kWPI; ++k) {
+            const f32x4 y = red[w + k][lane];
+            acc[0] += y[0]; acc[1] += y[1]; acc[2] += y[2]; acc[3] += y[3];
+        }
+    }
+    if (!live) return;
+    acc[0] *= inv; acc[1] *= inv; acc[2] *= inv; acc[3] *= inv;
+    *reinterpret_cast<bf16x4*>(op) = pack_bf16x4(acc);
+    if (half == 0 && lane == 0)
+        a.lse[(size_t)b * a.M + row] = tot > 0.f ? m_use + __log2f(tot) * kLn2 : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
-    const dim3 grid(plan.batch, (plan.M + kCombineRows - 1) / kCombineRows);
-    hipLaunchKernelGGL(mla_combine_kernel, grid, dim3(64 * kCombineRows), 0, stream, args);
+    // Partials per split sequence average about P / batch + 1; the waves
+    // sharing an item grow with that figure.
+    const int per_seq = plan.P / plan.batch;
+    const int items = 2 * plan.M;
+    if (per_seq >= 64) {
+        hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(plan.batch, items), dim3(64 * 16), 0, stream, args);
+    } else if (per_seq >= 16) {
+        hipLaunchKernelGGL(mla_combine_kernel<4>, dim3(plan.batch, items), dim3(64 * 4), 0, stream, args);
+    } else {
+        hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(plan.batch, (items + 3) / 4), dim3(64 * 4), 0, stream, args);
+    }
     return hipGetLastError();
 }
 

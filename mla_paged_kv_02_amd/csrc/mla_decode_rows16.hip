@@ -206,16 +206,22 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
 
         const int L = a.causal ? min(max(nseq - a.s_q + tok + 1, 0), nseq) : nseq;
         float m_ref = -INFINITY, l_run = 0.f;
+        // a segment holding the whole sequence writes the output itself;
+        // otherwise its partial goes to slot slot_base + (p - first partition)
+        const bool full = (lo == 0) && (hi == npages);
+        const int slotno = full ? 0 : ld_const_s(seqinfo, 4 * b + 0) + (p - ld_const_s(seqinfo, 4 * b + 1));
 
         // One page: the stripe of page pn sits in `cur`; the next page's
-        // stripe (or, past the segment end, a repeat of this one) is issued
-        // into `nxt` first, so exactly one stripe is always in flight.
-        // Returns the next page to process.
+        // stripe, if the segment has one, is issued into `nxt` first, so one
+        // stripe is in flight while this one is used. Returns the next page
+        // to process.
         auto page_step = [&](int pn, uint8_t* cur, uint32_t nxt_lds) -> int {
-            const int pn1 = pn + 1 < hi ? pn + 1 : pn;
-            issue_stripe(page_ptr(phys1), stripe_valid(pn1), nxt_lds);
+            const bool more = pn + 1 < hi;
+            if (more) issue_stripe(page_ptr(phys1), stripe_valid(pn + 1), nxt_lds);
             phys1 = ld_const_s(bt_row, pn + 2 < hi ? pn + 2 : hi - 1);
-            wait_then_fence<kWaitStripe>();   // this page's stripe and the table entry
+            // this page's stripe and the table entry
+            if (more) wait_then_fence<kWaitStripe>();
+            else wait_then_fence<kWaitAll>();
 
             // ---- S^T[key][row] = K Q^T over the stripe's 16 keys
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -303,8 +309,8 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
                 if (pn < 0 || pn >= hi) break;
             }
             restart = pn < 0;
-            // the last step's stripe (a repeat, or the page after a restart
-            // point) must land before the buffers are reused
+            // after a restart the stripe issued for the next page must land
+            // before the buffers are reused
             wait_then_fence<kWaitAll>();
             if (restart) {
                 issue_stripe(page_ptr(ld_const_s(bt_row, lo)), stripe_valid(lo), mine0_lds);
@@ -365,7 +371,6 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
                 res[t][0] += f * v[0]; res[t][1] += f * v[1]; res[t][2] += f * v[2]; res[t][3] += f * v[3];
             }
         }
-        const bool full = (lo == 0) && (hi == npages);
         if (row_ok) {
             const int col0 = wave * 128 + 4 * g;   // tile t covers columns col0 + 16 t .. +3
             if (full) {
@@ -376,7 +381,6 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
                 TileStores<8>::out(op, v);
                 if (wave == 0 && g == 0) a.lse[(size_t)b * a.M + row] = lse_v;
             } else {
-                const int slotno = ld_const_s(seqinfo, 4 * b + 0) + (p - ld_const_s(seqinfo, 4 * b + 1));
                 float* pp = a.part_o + ((size_t)slotno * a.M + row) * kHeadDimV + col0;
                 TileStores<8>::part(pp, res);
                 if (wave == 0 && g == 0) a.part_lse[(size_t)slotno * a.M + row] = lse_v;

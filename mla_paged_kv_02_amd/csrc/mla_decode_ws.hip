@@ -7,9 +7,11 @@
 // form). This organisation is for query blocks wide enough that the two
 // products and the LDS traffic that feeds them are the work:
 //
-//  * eight waves, two per SIMD. Score waves 0..3 own query rows 16s..16s+15
-//    (query in registers) and compute S^T = K Q^T, the mask and the softmax
-//    weights of every half page; value waves 4..7 own output columns
+//  * eight waves, two per SIMD. Score wave s owns key tile s & 1 (keys
+//    16(s&1)..+15 of every half page) for the 32 query rows of row tiles
+//    2(s>>1) and 2(s>>1)+1 (query in registers): each K fragment it reads
+//    from LDS feeds two row tiles. It computes S^T = K Q^T, the mask and the
+//    softmax weights of its keys. Value waves 4..7 own output columns
 //    128v..128v+127 of all 64 rows (O^T accumulators) and compute
 //    O^T += V^T P^T. P crosses over through LDS in exactly the MFMA operand
 //    layout, so each V^T fragment (two transposing LDS reads) feeds four row
@@ -17,15 +19,19 @@
 //    the value wave on the same SIMD keeps the matrix core busy;
 //  * the cache streams through a ring of four half-page slots (32 keys,
 //    36 KB): the value waves load them with 16-byte direct loads, two half
-//    pages ahead, while the score waves compute scores; a workgroup barrier
-//    starts each step (publishing a slot and the previous weights, freeing
-//    the slot the value waves finished) and one splits it in halves, so
-//    that 16-byte K reads and transposing V reads never share the LDS. Step
-//    c scores half page c and accumulates half page c-1;
-//  * softmax reference fixed per row at its first visible maximum plus a
-//    margin; a score beyond the headroom raises a flag that every wave reads
-//    after the next barrier, and the workgroup redoes the segment with raised
-//    references (exact; never triggered by scores of realistic range).
+//    pages ahead. Step c scores half page c and accumulates half page c-1;
+//    one workgroup barrier per step publishes half page c, the weights of
+//    half page c-1 and the overflow flags, and frees the slot the value
+//    waves finished;
+//  * the softmax reference of each row is fixed at its maximum over the
+//    first half page of the segment plus a margin: on that half page the
+//    score waves score both key tiles, so the two waves of a row pair take
+//    the same value without talking (the visible keys of a row are a prefix
+//    of the segment, so a row has no visible key later unless it has one
+//    there). A score beyond the headroom raises a flag that every wave reads
+//    after the next barrier; the workgroup merges the raised references of
+//    the two key tiles and redoes the segment (exact; never triggered by
+//    scores of realistic range).
 //
 // The direct-to-LDS loads are issued untracked by the compiler and every
 // wait for them is explicit. The two roles are separate code paths with the
@@ -65,7 +71,12 @@ __device__ __forceinline__ void wait_then_fence() {
     asm volatile("" ::: "memory");
 }
 
+// Workgroup barrier that publishes this wave's LDS writes: they have
+// completed (lgkmcnt(0)) before the wave arrives. Loads into LDS in flight
+// are not waited for here; their own waits precede the barrier that
+// publishes them.
 __device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -80,8 +91,10 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     // weights of a half page for the value waves: row tile rt at 1 KB * rt,
     // lane l at 16 l (the B operand of O^T += V^T P^T); two buffers by parity
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4 * 1024];
-    // per row of the block: softmax reference and sum, for the epilogue
-    __shared__ float row_ml[64][2];
+    // per row of the block: softmax reference, and the sums of the two key
+    // tiles, for the epilogue
+    __shared__ float row_m[64];
+    __shared__ float row_l[2][64];
     // overflow flags by step parity: set during step c in flag[c & 1], read
     // by every wave after the next barrier
     __shared__ int restart_flag[2];
@@ -159,10 +172,19 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     // waves' accumulators never live at the same program point.
     auto run = [&](auto role) {
         constexpr bool kScorer = decltype(role)::value;
-        const int srow = rb * 64 + sw * 16 + i16;   // score wave's query row
-        const bool srow_ok = srow < a.M;
-        const int stok = srow_ok ? srow / a.h_q : 0;
-        bf16x8 qf[kScorer ? kKS : 1];
+        // score wave: key tile kt, block rows lrow[r] = 32 rp + 16 r + i16
+        constexpr int NR = kScorer ? 2 : 1;
+        const int kt = sw & 1;
+        const int rp = sw >> 1;
+        int lrow[NR], stok[NR];
+        bool srow_ok[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            lrow[r] = 32 * rp + 16 * r + i16;
+            srow_ok[r] = rb * 64 + lrow[r] < a.M;
+            stok[r] = srow_ok[r] ? (rb * 64 + lrow[r]) / a.h_q : 0;
+        }
+        bf16x8 qf[NR][kScorer ? kKS : 1];
         f32x4 o[kScorer ? 1 : 4][kScorer ? 1 : kVTiles];
 
         int b = b0, n = n0;
@@ -185,13 +207,27 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 issue_half(page, cc & 1, nseq - (lo + cc / 2) * kPageRows, dst);
             };
 
-            const int L = a.causal ? min(max(nseq - a.s_q + stok + 1, 0), nseq) : nseq;
-            float m_ref = -INFINITY, l_run = 0.f;
-            if constexpr (kScorer) {
-                const uint16_t* qp =
-                    a.q + ((size_t)b * a.M + (srow_ok ? srow : rb * 64)) * kHeadDim + g * 8;
+            int L[NR];
+            float m_ref[NR], l_run[NR];
 #pragma unroll
-                for (int ks = 0; ks < kKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+            for (int r = 0; r < NR; ++r) {
+                L[r] = a.causal ? min(max(nseq - a.s_q + stok[r] + 1, 0), nseq) : nseq;
+                m_ref[r] = -INFINITY;
+                l_run[r] = 0.f;
+            }
+            // a segment holding the whole sequence writes the output itself;
+            // otherwise its partial goes to slot slot_base + (p - first partition)
+            const bool full = (lo == 0) && (hi == npages);
+            const int slotno =
+                full ? 0 : ld_const_ws(seqinfo, 4 * b + 0) + (p - ld_const_ws(seqinfo, 4 * b + 1));
+            if constexpr (kScorer) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const uint16_t* qp = a.q +
+                        ((size_t)b * a.M + (srow_ok[r] ? rb * 64 + lrow[r] : rb * 64)) * kHeadDim + g * 8;
+#pragma unroll
+                    for (int ks = 0; ks < kKS; ++ks) qf[r][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+                }
             }
 
             bool restart = false;
@@ -209,7 +245,8 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 #pragma unroll
                         for (int t = 0; t < kVTiles; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 } else {
-                    l_run = 0.f;
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) l_run[r] = 0.f;
                 }
                 block_barrier();   // every wave is past the previous use of the ring
                 if (restart && wid == 0 && lane == 0) {
@@ -218,15 +255,11 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
                 bool skip = false;   // overflow seen: no more weights until the restart
 
-                // Step c, first half: the value waves issue half page c+2
-                // into slot (S+2) % 4 (its previous contents, half page c-2,
-                // were accumulated in step c-1) while the score waves compute
-                // S^T for half page c from slot S = c % 4. Second half: the
-                // score waves turn the scores into weights while the value
-                // waves accumulate half page c-1 from slot (S+3) % 4. The
-                // 16-byte K reads and the transposing V reads stay in
-                // separate halves: concurrent transposing reads starve the
-                // others in the LDS.
+                // Step c: the value waves issue half page c+2 into slot
+                // (S+2) % 4 (its previous contents, half page c-2, were
+                // accumulated in step c-1) and accumulate half page c-1 from
+                // slot (S+3) % 4, while the score waves turn half page c
+                // (slot S = c % 4) into weights.
                 int c = 0;
                 auto step = [&](auto sc) -> bool {
                     constexpr int S = decltype(sc)::value;
@@ -234,89 +267,92 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                     if constexpr (!kScorer) {
                         wait_then_fence<kWaitSlot>();   // my part of half page c
                         page_next = page_of_chunk(c + 3);
-                    } else {
-                        // weights and flags of step c-1 are written
-                        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(63));
-                        asm volatile("" ::: "memory");
                     }
-                    block_barrier();
-                    const int flag = restart_flag[(S + 1) & 1];   // raised in step c-1; acted on below
-                    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+                    block_barrier();   // publishes the weights and flags of step c-1
+                    if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
                     if constexpr (!kScorer) {
                         issue_chunk(c + 2, page2, slot_lds[(S + 2) % 4]);
                         page2 = page_next;
                     } else if (c < nch) {
-                        const uint8_t* cur = slots[S];
-                        // ---- S^T = K Q^T, key tiles 0 and 1, two chains each
-                        f32x4 sp[2][2];
+                        // ---- S^T = K Q^T for key tile `tile` of half page c,
+                        // both row tiles; one K fragment feeds both. Lane
+                        // holds keys key0 + j (j < 4) of rows lrow[r], -inf
+                        // where masked; returns the row maxima (log2 domain).
+                        auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&mx)[NR]) {
+                            const uint8_t* kb = slots[S] + tile * 16 * kRowBytes;
+                            f32x4 sp[NR][2];
 #pragma unroll
-                        for (int kt = 0; kt < 2; ++kt)
+                            for (int r = 0; r < NR; ++r)
 #pragma unroll
-                            for (int pp = 0; pp < 2; ++pp) sp[kt][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        constexpr int KD = 4;
-                        auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
-                        bf16x8 k0[KD], k1[KD];
+                                for (int pp = 0; pp < 2; ++pp) sp[r][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+                            constexpr int KD = 4;
+                            auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
+                            bf16x8 kf[KD];
 #pragma unroll
-                        for (int d = 0; d < KD; ++d) {
-                            k0[d] = lds_read16(cur + k_off(d));
-                            k1[d] = lds_read16(cur + 16 * kRowBytes + k_off(d));
-                        }
+                            for (int d = 0; d < KD; ++d) kf[d] = lds_read16(kb + k_off(d));
 #pragma unroll
-                        for (int ks = 0; ks < kKS; ++ks) {
-                            sp[0][ks & 1] = mfma16(k0[ks % KD], qf[ks], sp[0][ks & 1]);
-                            sp[1][ks & 1] = mfma16(k1[ks % KD], qf[ks], sp[1][ks & 1]);
-                            if (ks + KD < kKS) {
-                                k0[ks % KD] = lds_read16(cur + k_off(ks + KD));
-                                k1[ks % KD] = lds_read16(cur + 16 * kRowBytes + k_off(ks + KD));
+                            for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+                                for (int r = 0; r < NR; ++r) sp[r][ks & 1] = mfma16(kf[ks % KD], qf[r][ks], sp[r][ks & 1]);
+                                if (ks + KD < kKS) kf[ks % KD] = lds_read16(kb + k_off(ks + KD));
+                                __builtin_amdgcn_sched_barrier(0);
                             }
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                        s0 = sp[0][0];
-                        s1 = sp[1][0];
+                            const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + tile * 16 + 4 * g;
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            s0[j] += sp[0][1][j];
-                            s1[j] += sp[1][1][j];
-                        }
-                    }
-                    block_barrier();   // the K reads of this step are done
-                    if (flag != 0) return false;
-                    if constexpr (kScorer) {
-                        if (c < nch) {
-                            // ---- mask + reference check; lane holds keys
-                            // 4g+j of key tile 0 and 16+4g+j of key tile 1
-                            const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + 4 * g;
-                            float mx = -INFINITY;
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const float v0 = (key0 + j < L) ? s0[j] * a.scale_log2 : -INFINITY;
-                                const float v1 = (key0 + 16 + j < L) ? s1[j] * a.scale_log2 : -INFINITY;
-                                s0[j] = v0;
-                                s1[j] = v1;
-                                mx = fmaxf(mx, fmaxf(v0, v1));
-                            }
-                            mx = max_over_kgroups(mx);
-                            if (m_ref == -INFINITY) m_ref = mx == -INFINITY ? -INFINITY : mx + kRefMargin;
-                            const bool over = mx > m_ref + kHeadroom;
-                            if (__ballot(over) != 0) {
-                                if (over) m_ref = mx + kRefMargin;
-                                if (lane == 0) restart_flag[S & 1] = 1;
-                                skip = true;
-                            }
-                            if (!skip) {
-                                const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+                            for (int r = 0; r < NR; ++r) {
+                                float m = -INFINITY;
 #pragma unroll
                                 for (int j = 0; j < 4; ++j) {
-                                    s0[j] = __builtin_amdgcn_exp2f(s0[j] - m_use);
-                                    s1[j] = __builtin_amdgcn_exp2f(s1[j] - m_use);
-                                    l_run += s0[j] + s1[j];
+                                    const float v = (key0 + j < L[r]) ? sp[r][0][j] + sp[r][1][j] : -INFINITY;
+                                    sv[r][j] = v;
+                                    m = fmaxf(m, v);
                                 }
-                                // B = P^T: k-slot j <-> key 4g+j, 4+j <-> key 16+4g+j
-                                *reinterpret_cast<bf16x8*>(&pbuf[S & 1][sw * 1024 + lane * 16]) =
-                                    cat_bf16x4(pack_bf16x4(s0), pack_bf16x4(s1));
+                                // scale > 0: the maximum commutes with it
+                                mx[r] = max_over_kgroups(m) * a.scale_log2;
+                            }
+                        };
+                        f32x4 sv[NR];
+                        float mx[NR];
+                        score_tile(kt, sv, mx);
+                        if (c == 0) {
+                            // the reference comes from both key tiles
+                            f32x4 so[NR];
+                            float mo[NR];
+                            score_tile(kt ^ 1, so, mo);
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) {
+                                mx[r] = fmaxf(mx[r], mo[r]);
+                                if (m_ref[r] == -INFINITY) m_ref[r] = mx[r] == -INFINITY ? -INFINITY : mx[r] + kRefMargin;
                             }
                         }
-                    } else if (c >= 1) {
+                        bool over = false;
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) over = over || (mx[r] > m_ref[r] + kHeadroom);
+                        if (__ballot(over) != 0) {
+#pragma unroll
+                            for (int r = 0; r < NR; ++r)
+                                if (mx[r] > m_ref[r] + kHeadroom) m_ref[r] = mx[r] + kRefMargin;
+                            if (lane == 0) restart_flag[S & 1] = 1;
+                            skip = true;
+                        }
+                        if (!skip) {
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) {
+                                const float neg_m = (m_ref[r] == -INFINITY) ? 0.f : -m_ref[r];
+                                f32x4 pw;
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    // masked scores are -inf: weight 0
+                                    pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r][j], a.scale_log2, neg_m));
+                                    l_run[r] += pw[j];
+                                }
+                                // B = P^T of row tile 2 rp + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j
+                                *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(2 * rp + r) * 1024 + lane * 16 + kt * 8]) =
+                                    pack_bf16x4(pw);
+                            }
+                        }
+                    }
+                    if (!kScorer && c >= 1) {
                         // ---- O^T += V^T P^T for half page c-1: four row tiles
                         // share each V^T fragment (two transposing reads)
                         const uint8_t* cur = slots[(S + 3) % 4];
@@ -355,23 +391,42 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 wait_then_fence<kWaitAll>();
                 block_barrier();
                 restart = (restart_flag[0] | restart_flag[1]) != 0;
-                if (restart) block_barrier();   // every wave has read the flag before it is cleared
+                if (restart) {
+                    // the two key tiles of a row pair raised their references
+                    // on their own scores: both take the larger one
+                    if constexpr (kScorer) {
+                        if (g == 0 && kt == 1)
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) row_m[lrow[r]] = m_ref[r];
+                    }
+                    block_barrier();
+                    if constexpr (kScorer) {
+                        if (kt == 0) {
+#pragma unroll
+                            for (int r = 0; r < NR; ++r) {
+                                m_ref[r] = fmaxf(m_ref[r], row_m[lrow[r]]);
+                                if (g == 0) row_m[lrow[r]] = m_ref[r];
+                            }
+                        }
+                    }
+                    block_barrier();
+                    if constexpr (kScorer) {
+#pragma unroll
+                        for (int r = 0; r < NR; ++r) m_ref[r] = row_m[lrow[r]];
+                    }
+                    block_barrier();   // every wave has read the flags and row_m
+                }
             } while (restart);
 
             // ---- epilogue: score waves publish (reference, sum) per row and
             // the lse; value waves normalise and store their columns
-            const bool full = (lo == 0) && (hi == npages);
-            int slotno = 0;
-            if (!full) slotno = ld_const_ws(seqinfo, 4 * b + 0) + (p - ld_const_ws(seqinfo, 4 * b + 1));
             if constexpr (kScorer) {
-                const float lsum = sum_over_kgroups(l_run);
-                if (g == 0) {
-                    row_ml[sw * 16 + i16][0] = m_ref;
-                    row_ml[sw * 16 + i16][1] = lsum;
-                    const float lse_v = lsum > 0.f ? (m_ref + __log2f(lsum)) * kLn2 : -INFINITY;
-                    if (srow_ok) {
-                        if (full) a.lse[(size_t)b * a.M + srow] = lse_v;
-                        else a.part_lse[(size_t)slotno * a.M + srow] = lse_v;
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const float lsum = sum_over_kgroups(l_run[r]);
+                    if (g == 0) {
+                        row_l[kt][lrow[r]] = lsum;
+                        if (kt == 0) row_m[lrow[r]] = m_ref[r];
                     }
                 }
             }
@@ -381,9 +436,15 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     const int row = rb * 64 + rt * 16 + i16;
-                    const float lsum = row_ml[rt * 16 + i16][1];
+                    const float lsum = row_l[0][rt * 16 + i16] + row_l[1][rt * 16 + i16];
                     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
                     if (row >= a.M) continue;
+                    if (sw == 0 && g == 0) {
+                        const float mr = row_m[rt * 16 + i16];
+                        const float lse_v = lsum > 0.f ? (mr + __log2f(lsum)) * kLn2 : -INFINITY;
+                        if (full) a.lse[(size_t)b * a.M + row] = lse_v;
+                        else a.part_lse[(size_t)slotno * a.M + row] = lse_v;
+                    }
                     if (full) {
                         uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + col0;
                         bf16x4 v[kVTiles];
@@ -406,7 +467,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                     }
                 }
             }
-            block_barrier();   // row_ml and the buffers are free again
+            block_barrier();   // row_m, row_l and the buffers are free again
             ++b;
             n = 0;
         }

@@ -8,6 +8,18 @@ namespace mla {
 namespace {
 
 constexpr int kSchedThreads = 1024;
+constexpr int kLdsBatch = 8192;   // 32 KB of cost-line starts
+
+// floor(a / b) through one correctly rounded double division. Exact for the
+// two quotients the plan needs: the numerator stays below 2^47 (a partition
+// index < 2^16 times a cost < 2^31) and the exact quotient q = n - k/b with
+// k >= 1 sits at least 1/b >= 2^-31 below the next integer, while the
+// rounding error is at most half an ulp of a quotient below 2^31 (<= 2^-22)
+// when b <= 2^16, or of a quotient below 2^16 (<= 2^-37) when b < 2^31.
+// The 64-bit integer division it replaces is a long instruction sequence.
+__device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
+    return (int64_t)__builtin_floor((double)a / (double)b);
+}
 
 // Exclusive prefix sum over the workgroup; *total receives the sum.
 __device__ int block_exclusive_scan(int v, int* total) {
@@ -36,6 +48,12 @@ __device__ int block_exclusive_scan(int v, int* total) {
 __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int32_t* seqlens,
                                                                        int batch, int P, int cseg,
                                                                        int32_t* meta) {
+    // cost-line starts stay in LDS for the boundary searches when they fit
+    // (every batch up to kLdsBatch sequences); larger batches search the copy
+    // in the metadata itself
+    __shared__ int32_t s_start[kLdsBatch];
+    __shared__ int32_t s_pages[kLdsBatch];
+    const bool in_lds = batch <= kLdsBatch;
     int32_t* seq = meta + kMetaHeader + 4 * P;
     const int tid = threadIdx.x;
 
@@ -43,10 +61,17 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     int carry = 0;
     for (int base = 0; base < batch; base += kSchedThreads) {
         const int b = base + tid;
-        const int v = b < batch ? (int)cost_len(seqlens[b], cseg) : 0;
+        const int32_t len = b < batch ? seqlens[b] : 0;
+        const int v = b < batch ? (int)cost_len(len, cseg) : 0;
         int chunk_total;
         const int ex = block_exclusive_scan(v, &chunk_total);
-        if (b < batch) seq[4 * b + 3] = carry + ex;
+        if (b < batch) {
+            seq[4 * b + 3] = carry + ex;
+            if (in_lds) {
+                s_start[b] = carry + ex;
+                s_pages[b] = pages_of(len);
+            }
+        }
         carry += chunk_total;
     }
     const int64_t total = carry;
@@ -57,7 +82,16 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     for (int base = 0; base < batch; base += kSchedThreads) {
         const int b = base + tid;
         int first = -1, count = 0;
-        if (b < batch) seq_partitions(seq[4 * b + 3], pages_of(seqlens[b]), cseg, total, pa, &first, &count);
+        if (b < batch) {
+            // both written by this thread above
+            const int32_t st = in_lds ? s_start[b] : seq[4 * b + 3];
+            const int32_t np = in_lds ? s_pages[b] : pages_of(seqlens[b]);
+            if (np > 0) {   // seq_partitions with the divisions above
+                first = (int32_t)floor_div((int64_t)(st + cseg + 1) * pa - 1, total);
+                const int32_t z = (int32_t)floor_div((int64_t)(st + cseg + np) * pa - 1, total);
+                count = z - first + 1;
+            }
+        }
         const int v = count > 1 ? count : 0;
         int chunk_total;
         const int ex = block_exclusive_scan(v, &chunk_total);
@@ -71,11 +105,14 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     __syncthreads();
 
     // partition boundaries
+    const int32_t* starts = in_lds ? s_start : seq + 3;
+    const int stride = in_lds ? 1 : 4;
     for (int p = tid; p < P; p += kSchedThreads) {
         int32_t* e = meta + kMetaHeader + 4 * p;
         if (p < pa) {
-            boundary_at(partition_start(p, total, pa), seq + 3, 4, batch, total, cseg, &e[0], &e[1]);
-            boundary_at(partition_start(p + 1, total, pa), seq + 3, 4, batch, total, cseg, &e[2], &e[3]);
+            // partition_start(p) = floor(p * total / pa)
+            boundary_at(floor_div((int64_t)p * total, pa), starts, stride, batch, total, cseg, &e[0], &e[1]);
+            boundary_at(floor_div((int64_t)(p + 1) * total, pa), starts, stride, batch, total, cseg, &e[2], &e[3]);
         } else {
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
         }

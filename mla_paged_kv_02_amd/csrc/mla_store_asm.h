@@ -1,12 +1,14 @@
 // mla_store_asm.h - epilogue stores of one wave's output row tiles.
 //
-// The stores are written as one inline-asm block that ends by waiting for
-// its own completion, so nothing it touches outlives the block. Keeping them
-// out of the compiler's view matters: it tracks store data registers on the
-// same counter as the direct-to-LDS loads, and a store-data register later
-// reused as the target of a transposing LDS read made it wait for every load
-// in flight before each such read. The epilogue runs once per sequence
-// segment, so its wait is cheap.
+// The stores are written as one inline-asm block so that the compiler does
+// not track them: it counts store-data registers on the same counter as the
+// direct-to-LDS loads, and a store-data register later reused as the target
+// of a transposing LDS read made it wait for every load in flight before each
+// such read. Nothing waits for the stores to complete: the data registers are
+// read when a store issues (the closing s_nop covers the one wait state a
+// VALU write to the data of a 16-byte store needs), and a vmcnt wait issued
+// later for younger loads stays exact, because loads complete in order, so
+// older stores can only make it wait longer.
 //
 // out tiles: tile t stores 4 BF16 values at p + 32*t bytes.
 // partial tiles: tile t stores 4 FP32 values at p + 64*t bytes.
@@ -30,7 +32,7 @@ struct TileStores<8> {
                      "global_store_dwordx2 %0, %6, off offset:160\n\t"
                      "global_store_dwordx2 %0, %7, off offset:192\n\t"
                      "global_store_dwordx2 %0, %8, off offset:224\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
                      : "memory");
@@ -44,7 +46,7 @@ struct TileStores<8> {
                      "global_store_dwordx4 %0, %6, off offset:320\n\t"
                      "global_store_dwordx4 %0, %7, off offset:384\n\t"
                      "global_store_dwordx4 %0, %8, off offset:448\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
                      : "memory");
@@ -70,7 +72,7 @@ struct TileStores<16> {
                      "global_store_dwordx2 %0, %14, off offset:416\n\t"
                      "global_store_dwordx2 %0, %15, off offset:448\n\t"
                      "global_store_dwordx2 %0, %16, off offset:480\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15])
                      : "memory");
@@ -92,7 +94,7 @@ struct TileStores<16> {
                      "global_store_dwordx4 %0, %14, off offset:832\n\t"
                      "global_store_dwordx4 %0, %15, off offset:896\n\t"
                      "global_store_dwordx4 %0, %16, off offset:960\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15])
                      : "memory");
@@ -134,7 +136,7 @@ struct TileStores<32> {
                      "global_store_dwordx2 %0, %30, off offset:928\n\t"
                      "global_store_dwordx2 %0, %31, off offset:960\n\t"
                      "global_store_dwordx2 %0, %32, off offset:992\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]), "v"(v[16]), "v"(v[17]), "v"(v[18]), "v"(v[19]), "v"(v[20]), "v"(v[21]), "v"(v[22]), "v"(v[23]), "v"(v[24]), "v"(v[25]), "v"(v[26]), "v"(v[27]), "v"(v[28]), "v"(v[29]), "v"(v[30]), "v"(v[31])
                      : "memory");
@@ -172,7 +174,7 @@ struct TileStores<32> {
                      "global_store_dwordx4 %0, %30, off offset:1856\n\t"
                      "global_store_dwordx4 %0, %31, off offset:1920\n\t"
                      "global_store_dwordx4 %0, %32, off offset:1984\n\t"
-                     "s_waitcnt vmcnt(0)"
+                     "s_nop 1"
                      :
                      : "v"(p), "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]), "v"(v[16]), "v"(v[17]), "v"(v[18]), "v"(v[19]), "v"(v[20]), "v"(v[21]), "v"(v[22]), "v"(v[23]), "v"(v[24]), "v"(v[25]), "v"(v[26]), "v"(v[27]), "v"(v[28]), "v"(v[29]), "v"(v[30]), "v"(v[31])
                      : "memory");

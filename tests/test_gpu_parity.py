@@ -117,6 +117,13 @@ def test_device_metadata_matches_host():
         host = mla.split_metadata_host(seqlens, h_q, s_q, host_parts)
         dev = meta.metadata.cpu().numpy()
         assert np.array_equal(dev, host), f"device metadata differs for h_q={h_q} parts={parts}"
+    # more sequences than the scheduler keeps in LDS, and cost lines long
+    # enough that partition arithmetic needs more than 32 bits
+    for batch, top, parts in [(9000, 3000, 4096), (64, 1 << 24, 60000), (3, 1 << 26, 65536)]:
+        seqlens = rng.integers(0, top, size=batch).astype(np.int32)
+        meta = mla.get_split_metadata(torch.from_numpy(seqlens).cuda(), 16, 1, parts)
+        host = mla.split_metadata_host(seqlens, 16, 1, parts)
+        assert np.array_equal(meta.metadata.cpu().numpy(), host), f"device metadata differs, batch={batch}"
 
 
 def test_run_to_run_bitwise():
