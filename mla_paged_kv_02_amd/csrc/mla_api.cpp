@@ -283,6 +283,7 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     a.seqlens = seqlens;
     a.meta = meta;
     a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
+    a.lse_stride = pl.slots;
     a.part_o = reinterpret_cast<float*>(ws + wl.o_off);
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;

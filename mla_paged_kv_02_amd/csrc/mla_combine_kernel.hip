@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
     }
     const int base = si.x;
     const int rr = live ? row : 0;
-    const float* lp = a.part_lse + (size_t)base * a.M + rr;
+    const float* lp = a.part_lse + (size_t)rr * a.lse_stride + base;   // lp[s]: partial s
 
     const float* pbase = a.part_o + ((size_t)base * a.M + rr) * kHeadDimV + col;
     const size_t pstride = (size_t)a.M * kHeadDimV;
@@ -74,18 +74,18 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
         const int su = sub + u * kWPI;
         if (su < cnt) {
             x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)su * pstride);
-            wt[u] = ld_const_f32(lp, (size_t)su * a.M);
+            wt[u] = ld_const_f32(lp, su);
         }
     }
 
     // combined lse (every wave of the item computes it; a few loads per lane)
     float m = -INFINITY;
-    for (int s = lane; s < cnt; s += 64) m = fmaxf(m, lp[(size_t)s * a.M]);
+    for (int s = lane; s < cnt; s += 64) m = fmaxf(m, lp[s]);
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, wave_xor(m, d));
     const float m_use = (m == -INFINITY) ? 0.f : m;
     float tot = 0.f;
-    for (int s = lane; s < cnt; s += 64) tot += __builtin_amdgcn_exp2f((lp[(size_t)s * a.M] - m_use) * kLog2e);
+    for (int s = lane; s < cnt; s += 64) tot += __builtin_amdgcn_exp2f((lp[s] - m_use) * kLog2e);
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) tot += wave_xor(tot, d);
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
@@ -103,13 +103,13 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
             x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)(s + u * kWPI) * pstride);
-            wt[u] = ld_const_f32(lp, (size_t)(s + u * kWPI) * a.M);
+            wt[u] = ld_const_f32(lp, s + u * kWPI);
         }
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) accumulate(x[u], wt[u]);
     }
     for (; s < cnt; s += kWPI) accumulate(*reinterpret_cast<const f32x4*>(pbase + (size_t)s * pstride),
-                                          ld_const_f32(lp, (size_t)s * a.M));
+                                          ld_const_f32(lp, s));
     if constexpr (kWPI > 1) {
         red[w][lane] = acc;
         __syncthreads();

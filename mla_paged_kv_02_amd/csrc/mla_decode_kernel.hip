@@ -378,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void mla_decode_kernel(DecodeArgs a) {
                     for (int dt = 0; dt < NDT; ++dt)
                         v[dt] = f32x4{o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv};
                     TileStores<NDT>::part(pp, v);
-                    if (cg == 0 && g == 0) a.part_lse[(size_t)slot * a.M + row] = lse_v;
+                    if (cg == 0 && g == 0) a.part_lse[(size_t)row * a.lse_stride + slot] = lse_v;
                 }
             }
         }

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
             } else {
                 float* pp = a.part_o + ((size_t)slotno * a.M + row) * kHeadDimV + col0;
                 TileStores<8>::part(pp, res);
-                if (wave == 0 && g == 0) a.part_lse[(size_t)slotno * a.M + row] = lse_v;
+                if (wave == 0 && g == 0) a.part_lse[(size_t)row * a.lse_stride + slotno] = lse_v;
             }
         }
         __syncthreads();   // buffers and the query block are free again

@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256) void mla_decode_wide_kernel(DecodeArgs a) {
                     v[dt][0] *= inv; v[dt][1] *= inv; v[dt][2] *= inv; v[dt][3] *= inv;
                 }
                 TileStores<kNDT>::part(pp, v);
-                if (g == 0) a.part_lse[(size_t)slotno * a.M + row[rt]] = lse_v;
+                if (g == 0) a.part_lse[(size_t)row[rt] * a.lse_stride + slotno] = lse_v;
             }
         }
         ++b;

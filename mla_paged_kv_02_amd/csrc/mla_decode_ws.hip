@@ -443,7 +443,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                         const float mr = row_m[rt * 16 + i16];
                         const float lse_v = lsum > 0.f ? (mr + __log2f(lsum)) * kLn2 : -INFINITY;
                         if (full) a.lse[(size_t)b * a.M + row] = lse_v;
-                        else a.part_lse[(size_t)slotno * a.M + row] = lse_v;
+                        else a.part_lse[(size_t)row * a.lse_stride + slotno] = lse_v;
                     }
                     if (full) {
                         uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + col0;

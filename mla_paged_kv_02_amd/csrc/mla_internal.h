@@ -19,6 +19,7 @@ struct Plan {
     DecodeKernel kernel;
     int tm, nw, nc;
     int R, P;
+    int lse_stride;    // split-partial slots of the plan
     int cseg;
     int slots;  // capacity of the split-partial buffers (sequence splits)
 };
@@ -43,12 +44,13 @@ struct DecodeArgs {
     const int32_t* seqlens;
     const int32_t* meta;
     float* part_o;
-    float* part_lse;
+    float* part_lse;   // row r, slot j at r * lse_stride + j: a row's partials are contiguous
     uint16_t* out;
     float* lse;
     int max_blocks;
     int batch, s_q, h_q, M;
     int R, P;
+    int lse_stride;    // split-partial slots of the plan
     float scale_log2;  // softmax_scale * log2(e)
     int causal;
 };
