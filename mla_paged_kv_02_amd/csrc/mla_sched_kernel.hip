@@ -21,27 +21,33 @@ __device__ __forceinline__ int64_t floor_div(int64_t a, int64_t b) {
     return (int64_t)__builtin_floor((double)a / (double)b);
 }
 
-// Exclusive prefix sum over the workgroup; *total receives the sum.
-__device__ int block_exclusive_scan(int v, int* total) {
-    __shared__ int wave_sums[kSchedThreads / 64];
+// Inclusive prefix sum over the 64 lanes of a wave with DPP lane moves:
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the last lane of
+// row 0 and of row 2 into rows 1 and 3, then the last lane of row 1 into rows
+// 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum over the workgroup; *total receives the sum. `sums`
+// holds the wave totals (kSchedThreads / 64 ints); a caller that scans again
+// before every wave is past this call's barrier passes another buffer.
+__device__ int block_exclusive_scan(int v, int* total, int* sums) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d, 64);
-        if (lane >= d) incl += t;
-    }
-    if (lane == 63) wave_sums[wave] = incl;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int incl = wave_inclusive_scan(v);
+    if (lane == 63) sums[wave] = incl;
     __syncthreads();
-    int offset = 0, sum = 0;
-    for (int w = 0; w < kSchedThreads / 64; ++w) {
-        const int ws = wave_sums[w];
-        if (w < wave) offset += ws;
-        sum += ws;
-    }
-    __syncthreads();
-    *total = sum;
+    constexpr int kWaves = kSchedThreads / 64;
+    const int ws = wave_inclusive_scan(lane < kWaves ? sums[lane] : 0);
+    *total = __builtin_amdgcn_readlane(ws, kWaves - 1);
+    const int offset = wave > 0 ? __builtin_amdgcn_readlane(ws, wave - 1) : 0;
     return offset + incl - v;
 }
 
@@ -53,18 +59,19 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     // in the metadata itself
     __shared__ int32_t s_start[kLdsBatch];
     __shared__ int32_t s_pages[kLdsBatch];
+    __shared__ int wave_sums[4][kSchedThreads / 64];   // scan totals, by call
     const bool in_lds = batch <= kLdsBatch;
     int32_t* seq = meta + kMetaHeader + 4 * P;
     const int tid = threadIdx.x;
 
     // cost-line start of every sequence
-    int carry = 0;
+    int carry = 0, nscan = 0;
     for (int base = 0; base < batch; base += kSchedThreads) {
         const int b = base + tid;
         const int32_t len = b < batch ? seqlens[b] : 0;
         const int v = b < batch ? (int)cost_len(len, cseg) : 0;
         int chunk_total;
-        const int ex = block_exclusive_scan(v, &chunk_total);
+        const int ex = block_exclusive_scan(v, &chunk_total, wave_sums[nscan++ & 3]);
         if (b < batch) {
             seq[4 * b + 3] = carry + ex;
             if (in_lds) {
@@ -94,7 +101,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
         }
         const int v = count > 1 ? count : 0;
         int chunk_total;
-        const int ex = block_exclusive_scan(v, &chunk_total);
+        const int ex = block_exclusive_scan(v, &chunk_total, wave_sums[nscan++ & 3]);
         if (b < batch) {
             seq[4 * b + 0] = count > 1 ? slots + ex : -1;
             seq[4 * b + 1] = first;
@@ -104,15 +111,35 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     }
     __syncthreads();
 
-    // partition boundaries
-    const int32_t* starts = in_lds ? s_start : seq + 3;
-    const int stride = in_lds ? 1 : 4;
+    // partition boundaries: boundary_at, searching the LDS copy of the
+    // starts when there is one
+    auto bound = [&](int64_t x, int32_t* b_out, int32_t* n_out) {
+        if (!in_lds) {
+            boundary_at(x, seq + 3, 4, batch, total, cseg, b_out, n_out);
+            return;
+        }
+        if (x >= total) {
+            *b_out = batch;
+            *n_out = 0;
+            return;
+        }
+        int lo = 0, hi = batch - 1;   // largest b with s_start[b] <= x
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_start[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        const int64_t off = x - s_start[lo] - cseg;
+        *b_out = lo;
+        *n_out = off < 0 ? 0 : (int32_t)off;
+    };
     for (int p = tid; p < P; p += kSchedThreads) {
         int32_t* e = meta + kMetaHeader + 4 * p;
         if (p < pa) {
             // partition_start(p) = floor(p * total / pa)
-            boundary_at(floor_div((int64_t)p * total, pa), starts, stride, batch, total, cseg, &e[0], &e[1]);
-            boundary_at(floor_div((int64_t)(p + 1) * total, pa), starts, stride, batch, total, cseg, &e[2], &e[3]);
+            int32_t v[4];
+            bound(floor_div((int64_t)p * total, pa), &v[0], &v[1]);
+            bound(floor_div((int64_t)(p + 1) * total, pa), &v[2], &v[3]);
+            e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
         } else {
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
         }
