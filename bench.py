@@ -31,17 +31,18 @@ from workloads import (MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, algorithm
 
 METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
 DEFAULT_WORKLOAD = "memory_bound"
-KERNEL_SOURCES = ["mla_decode_kernel.hip", "mla_combine_kernel.hip", "mla_common.h", "mla_sched.h",
-                  "mla_api.cpp", "mla_internal.h", "mla_sched_kernel.hip", "mla_store_asm.h",
-                  "mla_decode_rows16.hip"]
+CSRC = os.path.join(ROOT, "mla_paged_kv_02_amd", "csrc")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def kernel_digest() -> str:
+    """Digest of every library source (kernels, headers, host code)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "mla_paged_kv_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 

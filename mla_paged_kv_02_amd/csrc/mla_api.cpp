@@ -49,9 +49,7 @@ int kernel_override() {
         const char* e = std::getenv("MLA_DECODE_KERNEL");
         if (!e) return -1;
         if (!std::strcmp(e, "rows16")) return static_cast<int>(DecodeKernel::Rows16);
-        if (!std::strcmp(e, "wide")) return static_cast<int>(DecodeKernel::Wide);
         if (!std::strcmp(e, "ws")) return static_cast<int>(DecodeKernel::WaveSplit);
-        if (!std::strcmp(e, "ring")) return static_cast<int>(DecodeKernel::Ring);
         return -1;
     }();
     return v;
@@ -105,25 +103,14 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.h_q = h_q;
     pl.s_q = s_q;
     pl.M = (int)m;
-    // Kernel choice (MLA_DECODE_KERNEL=rows16|wide|ws|ring overrides it):
-    //   rows16: four waves split the keys of one 16-row block (M <= 64);
-    //   ws:     64-row blocks, four score waves and four value waves (M > 64);
-    //   wide:   64-row blocks, four waves of 16 rows doing both products;
-    //   ring:   32-row blocks, multi-row kernel with split value columns.
+    // Kernel choice (MLA_DECODE_KERNEL=rows16|ws overrides it): 16-row blocks
+    // while a sequence has at most 64 rows, 64-row blocks beyond.
     DecodeKernel k = pl.M <= 64 ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
     const int ov = kernel_override();
     if (ov >= 0) k = static_cast<DecodeKernel>(ov);
-    int tm = 16;
-    switch (k) {
-        case DecodeKernel::Rows16: tm = 16; break;
-        case DecodeKernel::Wide: tm = 64; break;
-        case DecodeKernel::WaveSplit: tm = 64; break;
-        case DecodeKernel::Ring: tm = 32; break;
-    }
+    const int tm = k == DecodeKernel::Rows16 ? 16 : 64;
     pl.kernel = k;
     pl.tm = tm;
-    pl.nw = 4;
-    pl.nc = k == DecodeKernel::Ring ? 2 : 0;
     pl.R = (pl.M + tm - 1) / tm;
     int p = num_partitions;
     if (p <= 0) {

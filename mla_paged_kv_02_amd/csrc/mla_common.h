@@ -29,9 +29,6 @@ constexpr float kLn2 = 0.6931471805599453f;
 // and inside the 72-chunk row.
 __device__ __forceinline__ int lds_swizzle(int row) { return row & 7; }
 
-__device__ __forceinline__ int lds_chunk_offset(int row, int chunk) {
-    return row * kRowBytes + ((chunk ^ lds_swizzle(row)) << 4);
-}
 
 // One 16-row x 16-column x 32-deep BF16 product, FP32 accumulate.
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -59,19 +56,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint8_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MLA_AS3 bf16x4*)(p));
 }
 
-// 16-byte direct load from global memory into LDS. Every lane of the wave
-// supplies its own source; the wave's 64 chunks land contiguously at `lds_dst`
-// (lane k at byte 16*k), which must be the same for all lanes.
-__device__ __forceinline__ void load_lds16(const void* src, void* lds_dst) {
-    __builtin_amdgcn_global_load_lds((const MLA_AS1 void*)(src), (MLA_AS3 void*)(lds_dst), 16, 0, 0);
-}
-
-// Same transfer, issued so that the compiler does not track it: the caller
-// owns every wait for it (s_waitcnt vmcnt before reading the destination, and
-// before reusing it). `base` is wave-uniform, `voff` the lane's byte offset
-// from it, `lds_addr` the LDS byte address of lane 0's chunk. Used where the
-// compiler's own tracking of direct-to-LDS loads cannot tell two buffers
-// apart and would drain every load in flight before each LDS read.
+// 16-byte direct load from global memory into LDS, issued so that the
+// compiler does not track it. Every lane supplies its own source (`base` is
+// wave-uniform, `voff` the lane's byte offset from it); the wave's 64 chunks
+// land contiguously from LDS byte address `lds_addr` (lane k at 16 k). The
+// caller owns every wait for it (s_waitcnt vmcnt before reading the
+// destination, and before reusing it): the compiler's own tracking of such
+// loads cannot tell two LDS buffers apart and would drain every load in
+// flight before each LDS read. M0 is named as clobbered: the kernels using
+// this helper have no other use of M0, so nothing the compiler keeps there
+// is lost.
 __device__ __forceinline__ void load_lds16_untracked(const void* base, uint32_t voff, uint32_t lds_addr) {
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
@@ -106,12 +100,6 @@ __device__ __forceinline__ float sum_over_kgroups(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 lo, f32x4 hi) {
-    bf16x8 r;
-    r[0] = (__bf16)lo[0]; r[1] = (__bf16)lo[1]; r[2] = (__bf16)lo[2]; r[3] = (__bf16)lo[3];
-    r[4] = (__bf16)hi[0]; r[5] = (__bf16)hi[1]; r[6] = (__bf16)hi[2]; r[7] = (__bf16)hi[3];
-    return r;
-}
 
 __device__ __forceinline__ bf16x4 pack_bf16x4(f32x4 v) {
     bf16x4 r;

@@ -7,19 +7,18 @@
 
 namespace mla {
 
-// How one decode call is cut into workgroups.
-//   rows per workgroup (tm) = 16 * waves / column groups
-//   every wave owns 16 query rows and 512/nc value columns
-//   R row blocks cover the M = h_q*s_q rows of a sequence; P partitions cut
-//   the page list; the grid is P*R workgroups.
-enum class DecodeKernel { Rows16, Wide, WaveSplit, Ring };
+// How one decode call is cut into workgroups: R row blocks of tm rows cover
+// the M = h_q*s_q rows of a sequence, P partitions cut the page list, and
+// the grid is P*R workgroups.
+//   Rows16:    tm = 16, four waves each owning a key stripe of every page;
+//   WaveSplit: tm = 64, four score waves and four value waves.
+enum class DecodeKernel { Rows16, WaveSplit };
 
 struct Plan {
     int batch, h_q, s_q, M;
     DecodeKernel kernel;
-    int tm, nw, nc;
+    int tm;
     int R, P;
-    int lse_stride;    // split-partial slots of the plan
     int cseg;
     int slots;  // capacity of the split-partial buffers (sequence splits)
 };
@@ -59,7 +58,6 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
                                  int32_t* meta, hipStream_t stream);
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
-hipError_t launch_decode_rows64(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 
