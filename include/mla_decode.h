@@ -140,7 +140,12 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
  *   causal         0 or 1 (bottom-right mask over the s_q new tokens)
  *   metadata       device buffer from mla_get_split_metadata for the same
  *                  seqlens/batch/h_q/s_q/num_partitions, or NULL to have this
- *                  call compute it inside `workspace` first
+ *                  call compute it inside `workspace` first. The plan itself
+ *                  is only read; its partial counters (one int per sequence
+ *                  and row block, zero as the metadata call writes them) are
+ *                  counted up during the call and left at zero again, so one
+ *                  metadata buffer serves any number of calls in stream
+ *                  order, but not two calls at the same time
  *   num_partitions the value given to mla_get_split_metadata (<= 0: default)
  *   workspace      device scratch, 16-byte aligned, of at least
  *                  mla_workspace_bytes(batch, h_q, s_q, num_partitions) bytes;
@@ -158,7 +163,7 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
 mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                           int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
                           int h_q, int num_pages, float softmax_scale, int causal,
-                          const int32_t* metadata, int num_partitions, void* workspace,
+                          int32_t* metadata, int num_partitions, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*

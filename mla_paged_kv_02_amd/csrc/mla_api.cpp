@@ -123,11 +123,22 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // page plus query load and output or partial traffic (~5 KB per row)
     pl.cseg = 1 + tm / 16;
     pl.slots = 2 * pl.P;
+    // With no more partitions than sequences most sequences sit in one
+    // partition and the few split ones have about two partials: the merge
+    // then runs in the decode kernel and the call is one kernel. With more
+    // partitions per sequence the merging workgroups' extra reads land on
+    // the critical path, and a combine kernel spreads them instead
+    // (MLA_COMBINE=kernel|fused, read at every call, overrides the choice).
+    pl.fused_combine = pl.P <= pl.batch;
+    if (const char* e = std::getenv("MLA_COMBINE")) {
+        if (!std::strcmp(e, "kernel")) pl.fused_combine = false;
+        if (!std::strcmp(e, "fused")) pl.fused_combine = true;
+    }
     *plan = pl;
     return true;
 }
 
-size_t metadata_bytes(const Plan& plan) { return (size_t)meta_ints(plan.batch, plan.P) * 4; }
+size_t metadata_bytes(const Plan& plan) { return (size_t)meta_ints(plan.batch, plan.P, plan.R) * 4; }
 
 WorkspaceLayout workspace_layout(const Plan& plan, bool with_metadata) {
     WorkspaceLayout w{};
@@ -204,7 +215,7 @@ mla_status mla_get_split_metadata(const int32_t* seqlens, int batch, int h_q, in
                    num_partitions > 0 ? 0 : current_cu_count(), &pl))
         return MLA_ERR_UNSUPPORTED;
     if (metadata_bytes_ < metadata_bytes(pl)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-    if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, metadata,
+    if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, pl.R, metadata,
                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
@@ -222,14 +233,14 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
                    num_partitions > 0 ? 0 : current_cu_count(), &pl))
         return MLA_ERR_UNSUPPORTED;
     if (metadata_bytes_ < metadata_bytes(pl)) return MLA_ERR_WORKSPACE_TOO_SMALL;
-    split_metadata_host(seqlens, batch, pl.P, pl.cseg, metadata);
+    split_metadata_host(seqlens, batch, pl.P, pl.cseg, pl.R, metadata);
     return MLA_OK;
 }
 
 mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
                           int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
                           int h_q, int num_pages, float softmax_scale, int causal,
-                          const int32_t* metadata, int num_partitions, void* workspace,
+                          int32_t* metadata, int num_partitions, void* workspace,
                           size_t workspace_bytes_, void* out, float* lse, void* stream) {
     if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse)
         return MLA_ERR_INVALID_ARG;
@@ -255,10 +266,10 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const int32_t* meta = metadata;
+    int32_t* meta = metadata;
     if (!meta) {
         int32_t* m = reinterpret_cast<int32_t*>(ws + wl.meta_off);
-        if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, m, st) != hipSuccess)
+        if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, pl.R, m, st) != hipSuccess)
             return MLA_ERR_HIP;
         meta = m;
     }
@@ -269,6 +280,7 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     a.block_table = block_table;
     a.seqlens = seqlens;
     a.meta = meta;
+    a.counters = pl.fused_combine ? meta + meta_counters(batch, pl.P) : nullptr;
     a.part_lse = reinterpret_cast<float*>(ws + wl.lse_off);
     a.lse_stride = pl.slots;
     a.part_o = reinterpret_cast<float*>(ws + wl.o_off);
@@ -287,7 +299,7 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     if (te && hipEventRecord(te->ev[0], st) != hipSuccess) return MLA_ERR_HIP;
     if (launch_decode(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
     if (te && hipEventRecord(te->ev[1], st) != hipSuccess) return MLA_ERR_HIP;
-    if (launch_combine(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
+    if (!pl.fused_combine && launch_combine(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
     if (te && hipEventRecord(te->ev[2], st) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }

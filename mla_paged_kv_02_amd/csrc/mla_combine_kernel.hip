@@ -35,10 +35,12 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
     constexpr int kWaves = kWPI > 4 ? kWPI : 4;
     constexpr int kItems = kWaves / kWPI;
     __shared__ f32x4 red[kWPI > 1 ? kWaves : 1][64];
-    const int b = blockIdx.x;
+    // one-dimensional grid, the blocks of a sequence consecutive
+    const int per_b = __builtin_amdgcn_readfirstlane((2 * a.M + kItems - 1) / kItems);
+    const int b = blockIdx.x / per_b;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int item = blockIdx.y * kItems + w / kWPI;   // row * 2 + half
+    const int item = (blockIdx.x - b * per_b) * kItems + w / kWPI;   // row * 2 + half
     const int sub = w % kWPI;
     const int row = item >> 1;
     const int half = item & 1;
@@ -132,14 +134,17 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
     // Partials per split sequence average about P / batch + 1; the waves
     // sharing an item grow with that figure.
+    // Consecutive blocks go to different XCDs, and a sequence's blocks are
+    // consecutive, so a long sequence's work spreads over all of them.
     const int per_seq = plan.P / plan.batch;
     const int items = 2 * plan.M;
+    const unsigned nb = (unsigned)plan.batch;
     if (per_seq >= 64) {
-        hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(plan.batch, items), dim3(64 * 16), 0, stream, args);
+        hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(nb * items), dim3(64 * 16), 0, stream, args);
     } else if (per_seq >= 16) {
-        hipLaunchKernelGGL(mla_combine_kernel<4>, dim3(plan.batch, items), dim3(64 * 4), 0, stream, args);
+        hipLaunchKernelGGL(mla_combine_kernel<4>, dim3(nb * items), dim3(64 * 4), 0, stream, args);
     } else {
-        hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(plan.batch, (items + 3) / 4), dim3(64 * 4), 0, stream, args);
+        hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(nb * ((items + 3) / 4)), dim3(64 * 4), 0, stream, args);
     }
     return hipGetLastError();
 }

@@ -30,6 +30,7 @@
 // them; every wait for them is explicit below (vmcnt counts are per wave, and
 // the wave issues nothing else to vector memory while a stripe is in flight).
 #include "mla_common.h"
+#include "mla_fused_combine.h"
 #include "mla_internal.h"
 #include "mla_sched.h"
 #include "mla_store_asm.h"
@@ -383,13 +384,19 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
             } else {
                 float* pp = a.part_o + ((size_t)slotno * a.M + row) * kHeadDimV + col0;
                 TileStores<8>::part(pp, res);
-                if (wave == 0 && g == 0) a.part_lse[(size_t)row * a.lse_stride + slotno] = lse_v;
+                if (wave == 0 && g == 0)   // device-coherent, as the partial tiles
+                    __hip_atomic_store(&a.part_lse[(size_t)row * a.lse_stride + slotno], lse_v, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         __syncthreads();   // buffers and the query block are free again
+        // the query buffer holds the flag: the next segment's query loads
+        // come after the helper's last barrier
+        if (!full && a.counters) count_partial_and_combine<256, 16>(a, b, rb, reinterpret_cast<int*>(qlds));
         ++b;
         n = 0;
     }
+    if (a.counters) write_empty_sequences<256>(a);
 }
 
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {

@@ -38,6 +38,7 @@
 // same barrier sequence, so the score waves' query registers and the value
 // waves' accumulators share the register file and two waves fit per SIMD.
 #include "mla_common.h"
+#include "mla_fused_combine.h"
 #include "mla_internal.h"
 #include "mla_sched.h"
 #include "mla_store_asm.h"
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     // overflow flags by step parity: set during step c in flag[c & 1], read
     // by every wave after the next barrier
     __shared__ int restart_flag[2];
+    __shared__ int last_flag;   // this workgroup merges a split sequence
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,23 +137,14 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
         const int c = k - r * kRowChunks;
         goff[j] = r * kRowBytes + ((c ^ lds_swizzle(r)) << 4);
     }
-    // Rows at or past the sequence end read the page's first kilobyte (row
-    // 0, always valid): finite data whose softmax weight is zero.
-    auto issue_half = [&](const uint8_t* page, int half, int valid, uint32_t dst) {
+    // Load j (of kWLoads) of this value wave's part of a half page. Rows at
+    // or past the sequence end read the page's first kilobyte (row 0, always
+    // valid): finite data whose softmax weight is zero.
+    auto issue_one = [&](const uint8_t* page, int half, int valid, uint32_t dst, int j) {
         const int base = half * kCBytes + sw * 9216;
-        const uint32_t d = dst + sw * 9216;
-        if (valid >= half * kCRows + sw * 8 + 8) {
-            const uint8_t* src = page + base;
-#pragma unroll
-            for (int j = 0; j < kWLoads; ++j) load_lds16_untracked(src, (uint32_t)goff[j], d + j * 1024);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kWLoads; ++j) {
-                const int r = half * kCRows + sw * 8 + (j * 64 + lane) / kRowChunks;
-                const uint32_t lo_off = r < valid ? (uint32_t)(base + goff[j]) : (uint32_t)(lane * 16);
-                load_lds16_untracked(page, lo_off, d + j * 1024);
-            }
-        }
+        const int r = half * kCRows + sw * 8 + (j * 64 + lane) / kRowChunks;
+        const uint32_t off = r < valid ? (uint32_t)(base + goff[j]) : (uint32_t)(lane * 16);
+        load_lds16_untracked(page, off, dst + sw * 9216 + j * 1024);
     };
 
     // per-lane LDS offsets inside a slot: K fragment of k-step ks for key row
@@ -202,13 +195,20 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 return reinterpret_cast<const uint8_t*>(a.kv) +
                        (size_t)ld_const_ws(bt_row, pn) * kPageBytes;
             };
-            auto issue_chunk = [&](int c, const uint8_t* page, uint32_t dst) {
+            // load j of half page c (past the segment end: the last one again,
+            // so that every step issues the same number of loads)
+            auto issue_part = [&](int c, const uint8_t* page, uint32_t dst, int j) {
                 const int cc = c < nch ? c : nch - 1;
-                issue_half(page, cc & 1, nseq - (lo + cc / 2) * kPageRows, dst);
+                issue_one(page, cc & 1, nseq - (lo + cc / 2) * kPageRows, dst, j);
+            };
+            auto issue_chunk = [&](int c, const uint8_t* page, uint32_t dst) {
+#pragma unroll
+                for (int j = 0; j < kWLoads; ++j) issue_part(c, page, dst, j);
             };
 
             int L[NR];
             float m_ref[NR], l_run[NR];
+            const float inv_scale = 1.f / a.scale_log2;
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 L[r] = a.causal ? min(max(nseq - a.s_q + stok[r] + 1, 0), nseq) : nseq;
@@ -270,15 +270,20 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                     }
                     block_barrier();   // publishes the weights and flags of step c-1
                     if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
+                    // value waves: half page c+2 into slot (S+2) % 4, which held
+                    // half page c-2 (accumulated in step c-1); spread over the
+                    // value products below, so the address unit that takes
+                    // the loads never backs the wave up for long
+                    const uint8_t* const page_c2 = page2;
                     if constexpr (!kScorer) {
-                        issue_chunk(c + 2, page2, slot_lds[(S + 2) % 4]);
                         page2 = page_next;
+                        if (c == 0) issue_chunk(c + 2, page_c2, slot_lds[(S + 2) % 4]);
                     } else if (c < nch) {
                         // ---- S^T = K Q^T for key tile `tile` of half page c,
                         // both row tiles; one K fragment feeds both. Lane
                         // holds keys key0 + j (j < 4) of rows lrow[r], -inf
-                        // where masked; returns the row maxima (log2 domain).
-                        auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&mx)[NR]) {
+                        // where masked; lm[r] = the lane's maximum of them.
+                        auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&lm)[NR]) {
                             const uint8_t* kb = slots[S] + tile * 16 * kRowBytes;
                             f32x4 sp[NR][2];
 #pragma unroll
@@ -307,31 +312,39 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                                     sv[r][j] = v;
                                     m = fmaxf(m, v);
                                 }
-                                // scale > 0: the maximum commutes with it
-                                mx[r] = max_over_kgroups(m) * a.scale_log2;
+                                lm[r] = m;
                             }
                         };
+                        // row maximum in the log2 domain (scale > 0: the
+                        // maximum commutes with it)
+                        auto row_max = [&](float m) { return max_over_kgroups(m) * a.scale_log2; };
                         f32x4 sv[NR];
-                        float mx[NR];
-                        score_tile(kt, sv, mx);
+                        float lm[NR];
+                        score_tile(kt, sv, lm);
                         if (c == 0) {
                             // the reference comes from both key tiles
                             f32x4 so[NR];
-                            float mo[NR];
-                            score_tile(kt ^ 1, so, mo);
+                            float lo2[NR];
+                            score_tile(kt ^ 1, so, lo2);
 #pragma unroll
                             for (int r = 0; r < NR; ++r) {
-                                mx[r] = fmaxf(mx[r], mo[r]);
-                                if (m_ref[r] == -INFINITY) m_ref[r] = mx[r] == -INFINITY ? -INFINITY : mx[r] + kRefMargin;
+                                const float mx = row_max(fmaxf(lm[r], lo2[r]));
+                                if (m_ref[r] == -INFINITY) m_ref[r] = mx == -INFINITY ? -INFINITY : mx + kRefMargin;
                             }
                         }
+                        // overflow: a score above the reference plus the
+                        // headroom, tested on raw scores against the limit
+                        // divided back by the scale (a bound, not a rounding
+                        // decision: weights stay below 2^64 either way)
                         bool over = false;
 #pragma unroll
-                        for (int r = 0; r < NR; ++r) over = over || (mx[r] > m_ref[r] + kHeadroom);
+                        for (int r = 0; r < NR; ++r) over = over || (lm[r] > (m_ref[r] + kHeadroom) * inv_scale);
                         if (__ballot(over) != 0) {
 #pragma unroll
-                            for (int r = 0; r < NR; ++r)
-                                if (mx[r] > m_ref[r] + kHeadroom) m_ref[r] = mx[r] + kRefMargin;
+                            for (int r = 0; r < NR; ++r) {
+                                const float mx = row_max(lm[r]);
+                                if (mx > m_ref[r] + kHeadroom) m_ref[r] = mx + kRefMargin;
+                            }
                             if (lane == 0) restart_flag[S & 1] = 1;
                             skip = true;
                         }
@@ -374,8 +387,11 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 #pragma unroll
                             for (int rt = 0; rt < 4; ++rt) o[rt][t] = mfma16(vf[t % VD], pf[rt], o[rt][t]);
                             if (t + VD < kVTiles) vf[t % VD] = v_frag(t + VD);
+                            issue_part(c + 2, page_c2, slot_lds[(S + 2) % 4], t);
                             __builtin_amdgcn_sched_barrier(0);
                         }
+                        static_assert(kVTiles + 1 == kWLoads, "one load per value tile and one after");
+                        issue_part(c + 2, page_c2, slot_lds[(S + 2) % 4], kVTiles);
                     }
                     ++c;
                     return c <= nch;
@@ -443,7 +459,9 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                         const float mr = row_m[rt * 16 + i16];
                         const float lse_v = lsum > 0.f ? (mr + __log2f(lsum)) * kLn2 : -INFINITY;
                         if (full) a.lse[(size_t)b * a.M + row] = lse_v;
-                        else a.part_lse[(size_t)row * a.lse_stride + slotno] = lse_v;
+                        else   // device-coherent, as the partial tiles
+                            __hip_atomic_store(&a.part_lse[(size_t)row * a.lse_stride + slotno], lse_v,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                     if (full) {
                         uint16_t* op = a.out + ((size_t)b * a.M + row) * kHeadDimV + col0;
@@ -468,9 +486,11 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
             }
             block_barrier();   // row_m, row_l and the buffers are free again
+            if (!full && a.counters) count_partial_and_combine<512, 64>(a, b, rb, &last_flag);
             ++b;
             n = 0;
         }
+        if (a.counters) write_empty_sequences<512>(a);
     };
     if (scorer) run(std::true_type{});
     else run(std::false_type{});

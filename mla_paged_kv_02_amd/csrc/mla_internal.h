@@ -21,6 +21,9 @@ struct Plan {
     int R, P;
     int cseg;
     int slots;  // capacity of the split-partial buffers (sequence splits)
+    // the last workgroup of a split sequence merges its partials (few
+    // partials per sequence); otherwise a combine kernel runs after decode
+    bool fused_combine;
 };
 
 // Returns false for unsupported shapes. num_partitions <= 0 selects the default.
@@ -42,6 +45,7 @@ struct DecodeArgs {
     const int32_t* block_table;
     const int32_t* seqlens;
     const int32_t* meta;
+    int32_t* counters;   // partial counters in the metadata; null when a combine kernel runs
     float* part_o;
     float* part_lse;   // row r, slot j at r * lse_stride + j: a row's partials are contiguous
     uint16_t* out;
@@ -55,7 +59,7 @@ struct DecodeArgs {
 };
 
 hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_partitions, int cseg,
-                                 int32_t* meta, hipStream_t stream);
+                                 int row_blocks, int32_t* meta, hipStream_t stream);
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
@@ -63,6 +67,6 @@ hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t 
 
 // Host build of the same plan (tests and host callers).
 void split_metadata_host(const int32_t* seqlens, int batch, int num_partitions, int cseg,
-                         int32_t* meta);
+                         int row_blocks, int32_t* meta);
 
 }  // namespace mla

@@ -53,7 +53,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* sums) {
 
 __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int32_t* seqlens,
                                                                        int batch, int P, int cseg,
-                                                                       int32_t* meta) {
+                                                                       int R, int32_t* meta) {
     // cost-line starts stay in LDS for the boundary searches when they fit
     // (every batch up to kLdsBatch sequences); larger batches search the copy
     // in the metadata itself
@@ -144,6 +144,8 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
         }
     }
+    // partial counters start at zero
+    for (int i = tid; i < R * batch; i += kSchedThreads) meta[meta_counters(batch, P) + i] = 0;
     if (tid < kMetaHeader) {
         int32_t h = 0;
         switch (tid) {
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
             case 5: h = slots; break;
             case 6: h = (int32_t)total; break;
             case 7: h = pa; break;
+            case 8: h = R; break;
             default: h = 0;
         }
         meta[tid] = h;
@@ -164,13 +167,13 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
 }  // namespace
 
 hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_partitions, int cseg,
-                                 int32_t* meta, hipStream_t stream) {
+                                 int row_blocks, int32_t* meta, hipStream_t stream) {
     hipLaunchKernelGGL(mla_split_meta_kernel, dim3(1), dim3(kSchedThreads), 0, stream, seqlens,
-                       batch, num_partitions, cseg, meta);
+                       batch, num_partitions, cseg, row_blocks, meta);
     return hipGetLastError();
 }
 
-void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int32_t* meta) {
+void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int R, int32_t* meta) {
     int32_t* seq = meta + kMetaHeader + 4 * P;
     int64_t total = 0;
     for (int b = 0; b < batch; ++b) {
@@ -205,6 +208,8 @@ void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int
     meta[5] = slots;
     meta[6] = (int32_t)total;
     meta[7] = pa;
+    meta[8] = R;
+    for (int i = 0; i < R * batch; ++i) meta[meta_counters(batch, P) + i] = 0;
 }
 
 }  // namespace mla

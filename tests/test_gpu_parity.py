@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import log, run_decode, score
+from gpu_util import bf16_bits_to_f64, log, run_decode, score
 from workloads import (WORKLOADS, make_inputs, make_workload_inputs, permute_pages,
                        poison_block_table_padding, poison_page_tails)
 
@@ -146,3 +146,39 @@ def test_named_workload_full_size(name):
     inp = make_workload_inputs(name)
     seqs = None if name == "tiny" else _sample_seqs(inp, 6)
     _check(inp, seqs=seqs, tag=f"workload {name}")
+
+
+@pytest.mark.parametrize("h_q,s_q,causal", [(16, 1, False), (128, 2, True)])
+def test_fused_combine_counters_and_modes(h_q, s_q, causal, monkeypatch):
+    """The merge inside the decode kernel (last workgroup of a split
+    sequence) against the combine kernel: same results, and the partial
+    counters in the metadata are zero again after every call, so repeated
+    calls with one metadata buffer agree."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from gpu_util import to_device
+    inp = make_inputs([0, 900, 3, 2049, 64, 1500, 0, 777], s_q, h_q, seed=31, causal=causal)
+    q, kv, bt, sl = to_device(inp)
+    ref_out, ref_lse = oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table,
+                                             inp.seqlens, inp.scale, inp.causal)
+    for parts in (8, 24):
+        meta = mla.get_split_metadata(sl, h_q, s_q, parts)
+        host = mla.split_metadata_host(inp.seqlens, h_q, s_q, parts)
+        results = {}
+        for mode in ("fused", "kernel", "fused"):
+            monkeypatch.setenv("MLA_COMBINE", mode)
+            out, lse = mla.decode_fwd(q, kv, bt, sl, inp.scale, inp.causal, meta=meta,
+                                      num_partitions=parts)
+            torch.cuda.synchronize()
+            bits = out.view(torch.int16).cpu().numpy().view(np.uint16)
+            lse_h = lse.cpu().numpy()
+            sc = score(bits, lse_h, ref_out, ref_lse)
+            log(f"[case] fused-combine h_q={h_q} parts={parts} mode={mode}: {sc}")
+            assert sc.ok(), f"{mode} parts={parts}: {sc}"
+            # the counters (and all of the plan) are as the metadata call wrote them
+            assert np.array_equal(meta.metadata.cpu().numpy(), host), f"metadata changed ({mode})"
+            if mode in results:
+                assert np.array_equal(results[mode][0], bits) and np.array_equal(results[mode][1], lse_h)
+            results[mode] = (bits, lse_h)
+        d = np.abs(bf16_bits_to_f64(results["fused"][0]) - bf16_bits_to_f64(results["kernel"][0]))
+        assert d.max() <= 2e-2
