@@ -49,7 +49,7 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
     // sequence record {slot base, first partition, partition count, cost start}
     typedef int i32x4 __attribute__((ext_vector_type(4)));
     const i32x4 si = reinterpret_cast<const __attribute__((address_space(4))) i32x4*>(
-        reinterpret_cast<uintptr_t>(a.meta + kMetaHeader + 4 * a.P))[b];
+        reinterpret_cast<uintptr_t>(a.meta + kMetaHeader + kPartInts * a.P))[b];
     const int cnt = si.z;
     if (cnt == 1) return;   // the decode kernel wrote this sequence's result
     const int col = half * 256 + lane * 4;

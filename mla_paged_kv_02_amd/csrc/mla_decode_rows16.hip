@@ -92,11 +92,16 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
     const int rb = (bid >> 3) % a.R;
     const int p = ((bid >> 3) / a.R) * 8 + (bid & 7);
 
-    int b = ld_const_s(a.meta, kMetaHeader + 4 * p + 0);
-    int n = ld_const_s(a.meta, kMetaHeader + 4 * p + 1);
-    const int b_end = ld_const_s(a.meta, kMetaHeader + 4 * p + 2);
-    const int n_end = ld_const_s(a.meta, kMetaHeader + 4 * p + 3);
-    const int32_t* seqinfo = a.meta + kMetaHeader + 4 * a.P;
+    // partition record: its range and the length of its first sequence,
+    // so that the first segment starts without another dependent load
+    const int32_t* part = a.meta + kMetaHeader + kPartInts * p;
+    int b = ld_const_s(part, 0);
+    int n = ld_const_s(part, 1);
+    const int b_end = ld_const_s(part, 2);
+    const int n_end = ld_const_s(part, 3);
+    const int len0 = ld_const_s(part, 4);
+    const int b_first = b;
+    const int32_t* seqinfo = a.meta + kMetaHeader + kPartInts * a.P;
 
     const int row = rb * 16 + i16;
     const bool row_ok = row < a.M;
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_kernel(DecodeArgs a) {
     const uint8_t* const q_frag = qlds + lane * 16;
 
     while (b < b_end || (b == b_end && n < n_end)) {
-        const int nseq = ld_const_s(a.seqlens, b);
+        const int nseq = b == b_first ? len0 : ld_const_s(a.seqlens, b);
         const int npages = pages_of(nseq);
         const int hi = (b == b_end) ? n_end : npages;
         if (n >= hi) { ++b; n = 0; continue; }

@@ -112,11 +112,15 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     const int rb = (bid >> 3) % a.R;
     const int p = ((bid >> 3) / a.R) * 8 + (bid & 7);
 
-    const int b0 = ld_const_ws(a.meta, kMetaHeader + 4 * p + 0);
-    const int n0 = ld_const_ws(a.meta, kMetaHeader + 4 * p + 1);
-    const int b_end = ld_const_ws(a.meta, kMetaHeader + 4 * p + 2);
-    const int n_end = ld_const_ws(a.meta, kMetaHeader + 4 * p + 3);
-    const int32_t* seqinfo = a.meta + kMetaHeader + 4 * a.P;
+    // partition record: its range and the length of its first sequence,
+    // so that the first segment starts without another dependent load
+    const int32_t* part = a.meta + kMetaHeader + kPartInts * p;
+    const int b0 = ld_const_ws(part, 0);
+    const int n0 = ld_const_ws(part, 1);
+    const int b_end = ld_const_ws(part, 2);
+    const int n_end = ld_const_ws(part, 3);
+    const int len0 = ld_const_ws(part, 4);
+    const int32_t* seqinfo = a.meta + kMetaHeader + kPartInts * a.P;
 
     if (threadIdx.x == 0) {
         restart_flag[0] = 0;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 
         int b = b0, n = n0;
         while (b < b_end || (b == b_end && n < n_end)) {
-            const int nseq = ld_const_ws(a.seqlens, b);
+            const int nseq = b == b0 ? len0 : ld_const_ws(a.seqlens, b);
             const int npages = pages_of(nseq);
             const int hi = (b == b_end) ? n_end : npages;
             if (n >= hi) { ++b; n = 0; continue; }

@@ -69,7 +69,7 @@ __device__ __forceinline__ void combine_rows(const DecodeArgs& a, int b, int row
 // no wave touches around the call. Every thread calls it.
 template <int kThreads, int kRows>
 __device__ __forceinline__ void count_partial_and_combine(const DecodeArgs& a, int b, int rb, int* flag) {
-    const int32_t* si = a.meta + kMetaHeader + 4 * a.P + 4 * b;
+    const int32_t* si = a.meta + kMetaHeader + kPartInts * a.P + 4 * b;
     const int base = si[0];
     const int cnt = si[2];
     // this thread's partial stores (device-coherent) have completed

@@ -19,13 +19,15 @@
 // Metadata layout (int32):
 //   [0]  magic   [1] batch   [2] P   [3] cseg   [4] ceil(T/P)   [5] total split slots
 //   [6]  total cost   [7] active partitions min(P, T)   [8] row blocks R   [9..15] zero
-//   [16 + 4p + {0,1,2,3}]           partition p: b_begin, n_begin, b_end, n_end
-//                                    (end exclusive, (b_end, 0) touches nothing of b_end)
-//   [16 + 4P + 4b + {0,1,2,3}]      sequence b: slot_base (-1 when not split),
+//   [16 + 8p + {0..7}]              partition p: b_begin, n_begin, b_end, n_end
+//                                    (end exclusive, (b_end, 0) touches nothing of
+//                                    b_end), the length of sequence b_begin (0 past
+//                                    the batch), three zeros
+//   [16 + 8P + 4b + {0,1,2,3}]      sequence b: slot_base (-1 when not split),
 //                                    first partition holding its pages (-1 if none),
 //                                    number of partitions holding its pages,
 //                                    start of the sequence on the cost line
-//   [16 + 4P + 4B + R b + rb]       partial counter of (sequence b, row block rb):
+//   [16 + 8P + 4B + R b + rb]       partial counter of (sequence b, row block rb):
 //                                    zero as written; the decode call counts the
 //                                    partials written into it and leaves it zero
 #pragma once
@@ -42,15 +44,16 @@ namespace mla {
 
 constexpr int32_t kMetaMagic = 0x314C4D41;  // "AML1"
 constexpr int kMetaHeader = 16;
+constexpr int kPartInts = 8;   // ints per partition record
 constexpr int kPageSize = 64;
 
 MLA_HD int meta_ints(int batch, int num_partitions, int row_blocks) {
-    return kMetaHeader + 4 * num_partitions + 4 * batch + row_blocks * batch;
+    return kMetaHeader + kPartInts * num_partitions + 4 * batch + row_blocks * batch;
 }
 
 // Offset of the partial counters.
 MLA_HD int meta_counters(int batch, int num_partitions) {
-    return kMetaHeader + 4 * num_partitions + 4 * batch;
+    return kMetaHeader + kPartInts * num_partitions + 4 * batch;
 }
 
 MLA_HD int32_t pages_of(int32_t seqlen) { return (seqlen + kPageSize - 1) / kPageSize; }

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     __shared__ int32_t s_pages[kLdsBatch];
     __shared__ int wave_sums[4][kSchedThreads / 64];   // scan totals, by call
     const bool in_lds = batch <= kLdsBatch;
-    int32_t* seq = meta + kMetaHeader + 4 * P;
+    int32_t* seq = meta + kMetaHeader + kPartInts * P;
     const int tid = threadIdx.x;
 
     // cost-line start of every sequence
@@ -133,16 +133,19 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
         *n_out = off < 0 ? 0 : (int32_t)off;
     };
     for (int p = tid; p < P; p += kSchedThreads) {
-        int32_t* e = meta + kMetaHeader + 4 * p;
+        int32_t* e = meta + kMetaHeader + kPartInts * p;
         if (p < pa) {
             // partition_start(p) = floor(p * total / pa)
             int32_t v[4];
             bound(floor_div((int64_t)p * total, pa), &v[0], &v[1]);
             bound(floor_div((int64_t)(p + 1) * total, pa), &v[2], &v[3]);
             e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
+            e[4] = v[0] < batch ? seqlens[v[0]] : 0;
         } else {
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
+            e[4] = 0;
         }
+        e[5] = 0; e[6] = 0; e[7] = 0;
     }
     // partial counters start at zero
     for (int i = tid; i < R * batch; i += kSchedThreads) meta[meta_counters(batch, P) + i] = 0;
@@ -174,7 +177,7 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
 }
 
 void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int R, int32_t* meta) {
-    int32_t* seq = meta + kMetaHeader + 4 * P;
+    int32_t* seq = meta + kMetaHeader + kPartInts * P;
     int64_t total = 0;
     for (int b = 0; b < batch; ++b) {
         seq[4 * b + 3] = (int32_t)total;
@@ -191,13 +194,16 @@ void split_metadata_host(const int32_t* seqlens, int batch, int P, int cseg, int
         if (count > 1) slots += count;
     }
     for (int p = 0; p < P; ++p) {
-        int32_t* e = meta + kMetaHeader + 4 * p;
+        int32_t* e = meta + kMetaHeader + kPartInts * p;
         if (p < pa) {
             boundary_at(partition_start(p, total, pa), seq + 3, 4, batch, total, cseg, &e[0], &e[1]);
             boundary_at(partition_start(p + 1, total, pa), seq + 3, 4, batch, total, cseg, &e[2], &e[3]);
+            e[4] = e[0] < batch ? seqlens[e[0]] : 0;
         } else {
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
+            e[4] = 0;
         }
+        e[5] = 0; e[6] = 0; e[7] = 0;
     }
     for (int i = 0; i < kMetaHeader; ++i) meta[i] = 0;
     meta[0] = kMetaMagic;

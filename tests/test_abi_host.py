@@ -46,8 +46,8 @@ def test_size_queries():
     assert lib.mla_metadata_bytes(0, 16, 1, 64) == 0          # batch < 1
     assert lib.mla_metadata_bytes(4, 0, 1, 64) == 0           # h_q < 1
     assert lib.mla_metadata_bytes(4, 512, 4, 64) == 0         # M > MLA_MAX_ROWS
-    assert lib.mla_metadata_bytes(4, 16, 1, 64) == 4 * (16 + 4 * 64 + 4 * 4 + 1 * 4)
-    assert lib.mla_metadata_bytes(4, 16, 1, 60) == 4 * (16 + 4 * 64 + 4 * 4 + 1 * 4)  # rounded to 8
+    assert lib.mla_metadata_bytes(4, 16, 1, 64) == 4 * (16 + 8 * 64 + 4 * 4 + 1 * 4)
+    assert lib.mla_metadata_bytes(4, 16, 1, 60) == 4 * (16 + 8 * 64 + 4 * 4 + 1 * 4)  # rounded to 8
     ws = lib.mla_workspace_bytes(4, 16, 1, 64)
     assert ws >= 2 * 64 * 16 * 512 * 4
 

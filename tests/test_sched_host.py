@@ -12,14 +12,17 @@ import pytest
 from mla_paged_kv_02_amd import split_metadata_host
 
 HEADER = 16
+PART_INTS = 8   # b_begin, n_begin, b_end, n_end, length of b_begin, 3 zeros
 
 
 def decode_plan(meta, batch):
     P = int(meta[2])
-    parts = meta[HEADER:HEADER + 4 * P].reshape(P, 4)
-    seq = meta[HEADER + 4 * P:HEADER + 4 * P + 4 * batch].reshape(batch, 4)
+    rec = meta[HEADER:HEADER + PART_INTS * P].reshape(P, PART_INTS)
+    parts = rec[:, :4]
+    seq = meta[HEADER + PART_INTS * P:HEADER + PART_INTS * P + 4 * batch].reshape(batch, 4)
     return dict(magic=int(meta[0]), batch=int(meta[1]), P=P, cseg=int(meta[3]), W=int(meta[4]),
-                slots=int(meta[5]), total=int(meta[6]), active=int(meta[7]), parts=parts, seq=seq)
+                slots=int(meta[5]), total=int(meta[6]), active=int(meta[7]), parts=parts, seq=seq,
+                first_len=rec[:, 4], pad=rec[:, 5:])
 
 
 def segments(plan, seqlens):
@@ -78,6 +81,11 @@ def check_plan(seqlens, h_q=16, s_q=1, nparts=64):
     assert plan["active"] == min(plan["P"], plan["total"])
     for p in range(plan["active"], plan["P"]):
         assert not any(s[0] == p for s in segs), "inactive partition got work"
+
+    # each record carries its first sequence's length (0 past the batch)
+    for p, (b0, _n0, _b1, _n1) in enumerate(plan["parts"]):
+        assert plan["first_len"][p] == (seqlens[b0] if b0 < len(seqlens) else 0)
+    assert not np.any(plan["pad"])
 
     # balance: no partition costs more than its share plus one extra segment
     cost = np.zeros(plan["P"], dtype=np.int64)
