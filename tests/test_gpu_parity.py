@@ -182,3 +182,33 @@ def test_fused_combine_counters_and_modes(h_q, s_q, causal, monkeypatch):
             results[mode] = (bits, lse_h)
         d = np.abs(bf16_bits_to_f64(results["fused"][0]) - bf16_bits_to_f64(results["kernel"][0]))
         assert d.max() <= 2e-2
+
+
+def _with_dominant_keys(inp, where, value_bits=0x4100):
+    """Overwrite the cache rows of (sequence, token) pairs in `where` with a
+    constant (8.0 by default) and the queries with 1.0: those keys score
+    ~2.8e2 in log2 units against ~1e1 for the others, far above the first
+    visible maximum plus the kernels' headroom, so every segment holding one
+    must raise its softmax reference and restart. Without that the weights
+    would overflow FP32."""
+    import dataclasses
+    q = np.full_like(inp.q_bits, 0x3F80)            # 1.0
+    kv = inp.kv_bits.copy()
+    for b, t in where:
+        phys = inp.block_table[b, t // 64]
+        kv[phys, t % 64, 0, :] = value_bits
+    return dataclasses.replace(inp, q_bits=q, kv_bits=kv)
+
+
+@pytest.mark.parametrize("h_q,s_q,causal,parts", [(16, 1, False, 0), (16, 1, False, 16),
+                                                  (64, 1, False, 0), (128, 2, True, 0),
+                                                  (128, 2, True, 24)])
+def test_reference_restart_on_dominant_key(h_q, s_q, causal, parts):
+    """A key whose score exceeds the row's first maximum by far more than the
+    headroom, late in the sequence (and, with splits, inside a later
+    partition): the kernels raise the reference and redo the segment; the
+    result must match the oracle (output ~ that key's value row)."""
+    inp = make_inputs([3000, 700, 150], s_q, h_q, seed=41 + parts, causal=causal)
+    inp = _with_dominant_keys(inp, [(0, 2500), (1, 600), (2, 100)])
+    out, lse = _check(inp, num_partitions=parts, tag=f"restart h_q={h_q} parts={parts}")
+    assert np.all(np.isfinite(lse))
