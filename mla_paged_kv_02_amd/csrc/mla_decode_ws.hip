@@ -104,7 +104,9 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool scorer = wid < kScoreWaves;
-    const int sw = wid & 3;   // score wave: row tile; value wave: column block
+    // score wave sw: key tile sw & 1 of row pair sw >> 1; value wave sw:
+    // column block sw (and rows 8 sw..8 sw+7 of every half page it loads)
+    const int sw = wid & 3;
     const int g = lane >> 4;
     const int i16 = lane & 15;
 
