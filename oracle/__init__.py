@@ -22,3 +22,4 @@ from .mla_ref import (  # noqa: F401
     mla_nonabsorbed_ref,
     mla_decode_bruteforce,
 )
+from .kv_append_ref import kv_append_ref  # noqa: F401

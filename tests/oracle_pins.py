@@ -193,3 +193,76 @@ def pin_two_keys(ref_f64):
     assert abs(out[0, 0, 0, 0] - (2 * w0 - 1)) < 1e-15
     assert abs(out[0, 0, 0, 1] - (2 * w0 + 5 * (1 - w0))) < 1e-14
     assert not np.any(out[0, 0, 0, 2:])
+
+
+# (k) Cache append, checked from the physical side: walk every block-table
+# entry and every slot of the page it names, work out which new token (if
+# any) the placement rule sends there, and require that row and nothing else
+# to change. Tokens with a position but no page are counted.
+def _append_cases(seed):
+    from workloads import make_append_inputs
+    cases = []
+    # ragged lengths around page edges; s_new larger than some sequences
+    a = make_append_inputs([0, 1, 5, 63, 64, 65, 130, 200], 70, seed, extra_blocks=1)
+    cases.append(a)
+    # holes in the table: a missing page (-1), an index past the cache, and a
+    # row too narrow for its sequence
+    b = make_append_inputs([150, 90, 300], 80, seed + 1)
+    t = b.block_table.copy()
+    t[0, 1] = -1
+    t[1, 0] = b.kv_bits.shape[0] + 3
+    b = type(b)(b.seqlens, t, b.kv_bits, b.new_bits)
+    cases.append(b)
+    c = make_append_inputs([100, 260], 40, seed + 2)
+    c = type(c)(c.seqlens, np.ascontiguousarray(c.block_table[:, :3]), c.kv_bits, c.new_bits)
+    cases.append(c)
+    return cases
+
+
+def pin_append_physical_view(append, seed=30):
+    for inp in _append_cases(seed):
+        kv_after, skipped = append(inp.kv_bits, inp.new_bits, inp.block_table, inp.seqlens)
+        expected = inp.kv_bits.copy()
+        num_pages = inp.kv_bits.shape[0]
+        s_new = inp.new_bits.shape[1]
+        written = 0
+        for b in range(inp.block_table.shape[0]):
+            first_new = int(inp.seqlens[b]) - s_new   # position of new token 0
+            for logical in range(inp.block_table.shape[1]):
+                page = int(inp.block_table[b, logical])
+                if not 0 <= page < num_pages:
+                    continue
+                for slot in range(PAGE):
+                    i = logical * PAGE + slot - first_new
+                    if 0 <= i < s_new:
+                        expected[page, slot, 0] = inp.new_bits[b, i]
+                        written += 1
+        placed = sum(min(int(n), s_new) for n in inp.seqlens)
+        assert np.array_equal(kv_after, expected), "append changed the wrong cache rows"
+        assert skipped == placed - written, f"skipped {skipped}, expected {placed - written}"
+
+
+# (l) Round trip: knock out the last s_new rows of every sequence in a full
+# cache and append them again; the cache must come back bit for bit, and
+# decode over it must match decode over the original.
+def pin_append_round_trip(append, seed=31, s_new=9):
+    inp = make_inputs([300, 64, 7, 129, 9], 1, 4, seed)
+    kv = inp.kv_bits
+    new = np.zeros((inp.batch, s_new, kv.shape[-1]), dtype=np.uint16)
+    damaged = kv.copy()
+    for b, n in enumerate(inp.seqlens):
+        n = int(n)
+        rows = oracle.gather_sequence_rows(kv, inp.block_table[b], n)
+        for i in range(s_new):
+            pos = n - s_new + i
+            if pos < 0:
+                new[b, i] = 0x3F80    # no place: must not be written anywhere
+                continue
+            new[b, i] = rows[pos]
+            damaged[inp.block_table[b, pos // PAGE], pos % PAGE, 0] = 0x7FC0
+    restored, skipped = append(damaged, new, inp.block_table, inp.seqlens)
+    assert skipped == 0
+    assert np.array_equal(restored, kv), "round trip did not restore the cache"
+    out0, lse0 = oracle.mla_decode_ref(inp.q_bits, kv, inp.block_table, inp.seqlens, inp.scale, False)
+    out1, lse1 = oracle.mla_decode_ref(inp.q_bits, restored, inp.block_table, inp.seqlens, inp.scale, False)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)

@@ -131,3 +131,66 @@ def test_layout_mutation_token_head_order_is_caught(monkeypatch):
 def test_combine_mutation_is_caught(monkeypatch):
     monkeypatch.setattr(R, "lse_combine_ref", _combine_plain_average)
     assert "combine" in _run_all_pins()
+
+
+# ---- cache append -----------------------------------------------------------
+
+def _append_variant(pos_fn=None, slot_fn=None, table_row_fn=None, keep_negative=False,
+                    count_negative=False, wrap_width=False):
+    """kv_append_ref with one step replaced."""
+    def append(kv_bits, new_bits, block_table, seqlens):
+        kv = np.array(kv_bits, copy=True)
+        bsz, s_new, _ = new_bits.shape
+        width = block_table.shape[1]
+        skipped = 0
+        for b in range(bsz):
+            n = int(seqlens[b])
+            for i in range(s_new):
+                pos = pos_fn(n, s_new, i) if pos_fn else n - s_new + i
+                if pos < 0 and not keep_negative:
+                    if count_negative:
+                        skipped += 1
+                    continue
+                logical = pos // 64
+                row = table_row_fn(b) if table_row_fn else b
+                if wrap_width:
+                    page = int(block_table[row, logical % width])
+                else:
+                    page = int(block_table[row, logical]) if logical < width else -1
+                if page < 0 or page >= kv.shape[0]:
+                    skipped += 1
+                    continue
+                slot = slot_fn(pos, i) if slot_fn else pos % 64
+                kv[page, slot, 0, :] = new_bits[b, i, :]
+        return kv, skipped
+    return append
+
+
+APPEND_MUTATIONS = {
+    "position_off_by_one": _append_variant(pos_fn=lambda n, s, i: n - s + i + 1),
+    "position_from_start": _append_variant(pos_fn=lambda n, s, i: i),
+    "negative_positions_written": _append_variant(keep_negative=True),
+    "negative_positions_counted": _append_variant(count_negative=True),
+    "slot_from_token_index": _append_variant(slot_fn=lambda pos, i: i % 64),
+    "first_sequence_table_row": _append_variant(table_row_fn=lambda b: 0),
+    "table_index_wraps": _append_variant(wrap_width=True),
+}
+
+
+def _run_append_pins(fn):
+    failed = []
+    for name, pin in [("physical", P.pin_append_physical_view), ("round_trip", P.pin_append_round_trip)]:
+        try:
+            pin(fn)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_append_passes_its_pins():
+    assert _run_append_pins(oracle.kv_append_ref) == []
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_MUTATIONS))
+def test_append_mutation_is_caught(name):
+    assert _run_append_pins(APPEND_MUTATIONS[name]), f"append mutation {name} passed every pin"

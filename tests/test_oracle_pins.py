@@ -38,3 +38,11 @@ def test_bounds():
 
 def test_two_keys_by_hand():
     P.pin_two_keys(oracle.mla_decode_ref_f64)
+
+
+def test_append_physical_view():
+    P.pin_append_physical_view(oracle.kv_append_ref)
+
+
+def test_append_round_trip():
+    P.pin_append_round_trip(oracle.kv_append_ref)

@@ -21,6 +21,10 @@ from .gen import (  # noqa: F401
     permute_pages,
     poison_page_tails,
     poison_block_table_padding,
+    AppendInputs,
+    APPEND_WORKLOADS,
+    make_append_inputs,
+    make_append_workload,
 )
 from .roofline import (  # noqa: F401
     algorithmic_bytes,

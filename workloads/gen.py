@@ -208,3 +208,52 @@ def poison_block_table_padding(inp: MlaInputs) -> MlaInputs:
             vals = np.where(np.arange(pad) % 2 == 0, -1, np.iinfo(np.int32).max)
             table[b, used:] = vals.astype(np.int32)
     return dataclasses.replace(inp, block_table=table)
+
+
+@dataclasses.dataclass
+class AppendInputs:
+    """Host-side inputs of a cache append. BF16 tensors as uint16 bits."""
+
+    seqlens: np.ndarray        # int32 [B], lengths after the append
+    block_table: np.ndarray    # int32 [B, max_blocks]
+    kv_bits: np.ndarray        # uint16 [NB, 64, 1, 576], the cache before the append
+    new_bits: np.ndarray       # uint16 [B, s_new, 576]
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+    @property
+    def s_new(self) -> int:
+        return int(self.new_bits.shape[1])
+
+
+def make_append_inputs(seqlens: Sequence[int], s_new: int, seed: int,
+                       extra_blocks: int = 0) -> AppendInputs:
+    """Pages, block table and prior cache content as for decode (steps 1-4 of
+    the recipe, with one query head and token), then the new rows
+    ``rng.standard_normal((B, s_new, 576))`` rounded to BF16 from the same
+    stream."""
+    rng = np.random.default_rng(seed)
+    base = make_inputs(seqlens, 1, 1, seed, rng=rng, extra_blocks=extra_blocks)
+    new_bits = _standard_normal_bf16(rng, (base.batch, s_new, HEAD_DIM))
+    return AppendInputs(base.seqlens, base.block_table, base.kv_bits, new_bits)
+
+
+# Append workloads: the rows of one decode step of the memory-bound workload,
+# and one chunk of chunked prefill (2048 new tokens for each of 32 sequences
+# that end up 2048..8192 tokens long).
+APPEND_WORKLOADS = {
+    "append_decode_step": dict(s_new=1, seed=21, lengths=("uniform", 64, 3072, 5120)),
+    "append_prefill_chunk": dict(s_new=2048, seed=22, lengths=("uniform", 32, 2048, 8192)),
+}
+
+
+def make_append_workload(name: str) -> AppendInputs:
+    w = APPEND_WORKLOADS[name]
+    rng = np.random.default_rng(w["seed"])
+    _, n, lo, hi = w["lengths"]
+    seqlens = rng.integers(lo, hi, size=n, endpoint=True).astype(np.int32)
+    base = make_inputs(seqlens, 1, 1, w["seed"], rng=rng)
+    new_bits = _standard_normal_bf16(rng, (n, w["s_new"], HEAD_DIM))
+    return AppendInputs(base.seqlens, base.block_table, base.kv_bits, new_bits)
