@@ -27,7 +27,7 @@ HEAD_DIM = 576
 HEAD_DIM_V = 512
 PAGE_SIZE = 64
 
-__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "split_metadata_host",
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "kv_append", "split_metadata_host",
            "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
 
 
@@ -166,6 +166,40 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
     check(status, "mla_decode_fwd")
     return out, lse
+
+
+def kv_append(new_rows: torch.Tensor, seqlens: torch.Tensor, block_table: torch.Tensor,
+              kv_cache: torch.Tensor, skipped: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Write the new tokens' cache rows into the paged cache (mla_kv_append).
+
+    new_rows [B, s_new, 576] bf16; seqlens [B] int32 holds the cache lengths
+    after the append (token i of sequence b lands at position
+    N_b - s_new + i); block_table [B, max_blocks] int32; kv_cache
+    [num_pages, 64, 1, 576] (or [num_pages, 64, 576]) bf16, updated in place.
+    ``skipped`` (int32 scalar tensor, optional) is incremented for each token
+    whose page is missing from the table. Returns kv_cache.
+    """
+    dev = new_rows.device
+    _require(new_rows, "new_rows", torch.bfloat16, ndim=3)
+    bsz, s_new, d = new_rows.shape
+    if d != HEAD_DIM:
+        raise ValueError(f"new_rows head dim must be {HEAD_DIM}, got {d}")
+    _require(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    if tuple(kv_cache.shape[1:]) not in ((PAGE_SIZE, 1, HEAD_DIM), (PAGE_SIZE, HEAD_DIM)):
+        raise ValueError(f"kv_cache must be [num_pages, 64, 1, 576], got {tuple(kv_cache.shape)}")
+    _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
+    _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != bsz or seqlens.shape[0] != bsz:
+        raise ValueError("block_table and seqlens must have one row per sequence")
+    if skipped is not None:
+        _require(skipped, "skipped", torch.int32, device=dev)
+        if skipped.numel() != 1:
+            raise ValueError("skipped must hold one int32")
+    check(lib().mla_kv_append(new_rows.data_ptr(), bsz, s_new, seqlens.data_ptr(), block_table.data_ptr(),
+                              block_table.shape[1], kv_cache.data_ptr(), kv_cache.shape[0],
+                              skipped.data_ptr() if skipped is not None else None, _stream_ptr(dev)),
+          "mla_kv_append")
+    return kv_cache
 
 
 def timing_enable(enable: bool = True) -> None:

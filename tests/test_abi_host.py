@@ -11,20 +11,24 @@ import pytest
 from mla_paged_kv_02_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, INVALID, UNSUPPORTED, MISALIGNED, TOO_SMALL, HIP = range(6)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_two_calls():
     names = declared_functions()
     assert "mla_get_split_metadata" in names and "mla_decode_fwd" in names
+    assert "mla_kv_append" in names
 
 
 def test_library_exports_every_declared_symbol():
@@ -109,3 +113,24 @@ def test_timing_record_is_empty_without_calls():
     assert (d.value, c.value, n.value) == (0.0, 0.0, 0)
     assert lib.mla_timing_collect(None, None, None) == OK
     assert lib.mla_timing_enable(0) == OK
+
+
+def _append(**kw):
+    args = dict(new=FAKE, batch=2, s_new=3, seqlens=FAKE, bt=FAKE, maxb=4, kv=FAKE, pages=8,
+                skipped=None, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_kv_append(args["new"], args["batch"], args["s_new"], args["seqlens"],
+                                    args["bt"], args["maxb"], args["kv"], args["pages"],
+                                    args["skipped"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(new=None), INVALID), (dict(seqlens=None), INVALID), (dict(bt=None), INVALID),
+    (dict(kv=None), INVALID), (dict(batch=0), INVALID), (dict(s_new=0), INVALID),
+    (dict(maxb=0), INVALID), (dict(pages=0), INVALID),
+    (dict(batch=1 << 16, s_new=1 << 15), UNSUPPORTED),
+    (dict(new=FAKE + 8), MISALIGNED), (dict(kv=FAKE + 2), MISALIGNED), (dict(bt=FAKE + 2), MISALIGNED),
+    (dict(seqlens=FAKE + 1), MISALIGNED), (dict(skipped=FAKE + 2), MISALIGNED),
+])
+def test_append_argument_checks(kw, status):
+    assert _append(**kw) == status

@@ -41,6 +41,11 @@ SMALL_CASES = [
     ([90, 45], 1, 24, False),          # rows not a multiple of 16
     ([150], 3, 8, True),               # M = 24, three causal tokens
     ([1000, 17], 1, 16, True),         # causal with s_q = 1 is a no-op
+    # larger S_q (speculative / chunked decode), up to the row limit M = 1024
+    ([150, 3, 1000, 64], 8, 128, True),
+    ([500, 20, 64, 0], 64, 16, True),
+    ([300, 2, 77], 16, 64, False),
+    ([40, 129], 32, 8, True),
 ]
 
 
