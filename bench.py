@@ -26,8 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS, algorithmic_bytes,  # noqa: E402
-                       algorithmic_flops, make_workload_inputs)
+from workloads import (APPEND_WORKLOADS, MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS,  # noqa: E402
+                       algorithmic_bytes, algorithmic_flops, make_append_workload, make_workload_inputs)
 
 METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
 DEFAULT_WORKLOAD = "memory_bound"
@@ -35,10 +35,21 @@ CSRC = os.path.join(ROOT, "mla_paged_kv_02_amd", "csrc")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_digest() -> str:
-    """Digest of every library source (kernels, headers, host code)."""
+# Sources of the cache-append op; the decode path's digest leaves them out,
+# so that changing one does not void the other's counter figures.
+APPEND_SOURCES = ("mla_kv_append.hip", "mla_common.h")
+
+
+def kernel_digest(op: str = "decode") -> str:
+    """Digest of the library sources an op's kernels are built from: every
+    source but the append kernel for decode, the append kernel and the shared
+    constants for kv_append."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
+        if op == "kv_append" and f not in APPEND_SOURCES:
+            continue
+        if op == "decode" and f == APPEND_SOURCES[0]:
+            continue
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
@@ -46,18 +57,63 @@ def kernel_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per decode call from the committed rocprofv3 counter runs,
-    or None when absent or taken on different kernel sources."""
+def counter_entry(workload: str):
+    """The committed rocprofv3 counter figures of `workload` (HBM bytes and
+    MFMA ops per decode call), or None when absent or taken on different
+    kernel sources."""
     try:
         with open(COUNTERS_FILE) as f:
             doc = json.load(f)
     except (OSError, ValueError):
         return None
     entry = doc.get("workloads", {}).get(workload)
-    if not entry or entry.get("kernel_digest") != kernel_digest():
+    if not entry or entry.get("kernel_digest") != kernel_digest(_op_of(workload)):
         return None
-    return entry.get("bytes_per_call")
+    return entry
+
+
+def _op_of(workload: str) -> str:
+    return "kv_append" if workload in APPEND_WORKLOADS else "decode"
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def streaming_context(nbytes: int = 1 << 30, reps: int = 10):
+    """What plain torch kernels reach on this GPU, as context next to the
+    datasheet peak: a full reduction that reads `nbytes` once, and a copy of
+    `nbytes` (read + write). Median over `reps` event-timed runs."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    s = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e-3
+
+    t_read = timed(lambda: torch.sum(x, dim=0, out=s))
+    t_copy = timed(lambda: y.copy_(x))
+    del x, y
+    return {"bytes": nbytes, "torch_sum_read_gbps": round(nbytes / t_read / 1e9, 1),
+            "torch_copy_gbps": round(2 * nbytes / t_copy / 1e9, 1)}
 
 
 def cpu_baseline(workload: str, inp, budget_s: float):
@@ -87,7 +143,10 @@ def cpu_baseline(workload: str, inp, budget_s: float):
             "kind": "oracle",
             "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {inp.batch}-sequence "
                       f"batch, {int(inp.seqlens[done].sum())} tokens) in {dt:.1f} s; numpy FP64 "
-                      f"two-pass softmax per sequence, GB/s from the same algorithmic-bytes formula"}
+                      f"two-pass softmax per sequence, GB/s from the same algorithmic-bytes formula",
+            "seconds": round(dt, 2),
+            "cpu_model": cpu_model(),
+            "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_bytes: int,
@@ -112,6 +171,8 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     stream = torch.cuda.current_stream(dev)
 
     def step(i, ev=None):
+        if ev is not None:
+            ev[2].record(stream)
         meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions)
         if ev is not None:
             ev[0].record(stream)
@@ -136,8 +197,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     # (2) per-kernel durations: the library records HIP events on this stream
     # around each decode and each combine kernel; torch events bracket each
     # decode_fwd call. A separate pass, since the markers add dispatch gaps.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     mla.timing_enable(True)
     for i in range(steps):
         step(i, evs[i])
@@ -145,7 +205,8 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     dec_ms_sum, comb_ms_sum, ncalls = mla.timing_collect()
     mla.timing_enable(False)
     assert ncalls == steps, f"timed {ncalls} calls, expected {steps}"
-    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    meta_ms = np.array([e[2].elapsed_time(e[0]) for e in evs])
     call_ms_mean = float(call_ms.mean())
     dec_ms = dec_ms_sum / steps
     comb_ms = comb_ms_sum / steps
@@ -159,7 +220,8 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     dec_gbps = nbytes / (dec_ms * 1e-3) / 1e9
     dec_tflops = flops / (dec_ms * 1e-3) / 1e12
     hbm_bound = nbytes * 1.0 / (MI355X_HBM_GBPS * 1e9) >= flops * 1.0 / (MI355X_BF16_TFLOPS * 1e12)
-    traffic = counter_traffic(name)
+    cnt = counter_entry(name)
+    traffic = cnt.get("bytes_per_call") if cnt else None
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": MI355X_HBM_GBPS,
                 "unit": "GB/s", "frac": round(dec_gbps / MI355X_HBM_GBPS, 4),
@@ -189,7 +251,10 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         "hbm_frac_of_peak": round(gbps / MI355X_HBM_GBPS, 4),
         "mfma_frac_of_peak": round(tflops / MI355X_BF16_TFLOPS, 4),
         "decode_call_us": round(call_ms_mean * 1e3, 2),
+        "decode_call_us_median": round(float(np.median(call_ms)) * 1e3, 2),
         "decode_call_us_min": round(float(call_ms.min()) * 1e3, 2),
+        "decode_call_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2),
+        "metadata_us_median": round(float(np.median(meta_ms)) * 1e3, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
         "algorithmic_bytes": nbytes,
@@ -198,9 +263,92 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         "roofline": roof,
         "kernel_digest": kernel_digest(),
     }
+    if cnt:
+        c = {"hbm_bytes_per_call": traffic,
+             "bytes_over_algorithmic": round(traffic / nbytes, 3) if traffic else None}
+        if cnt.get("mfma_mops_bf16_per_call"):
+            mf = cnt["mfma_mops_bf16_per_call"] * 512
+            c.update({"mfma_flops_per_call": mf, "flops_over_algorithmic": round(mf / flops, 3)})
+        line["counters"] = c
     if cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(name, inp, cpu_budget)
     return line
+
+
+def append_bytes(inp) -> int:
+    """Algorithmic bytes of one cache append: each placed token's row read once
+    and written once (2 x 1152 B), one block-table entry per (sequence, page)
+    touched, and the lengths."""
+    s_new = inp.s_new
+    rows, pages = 0, 0
+    for n in inp.seqlens:
+        n = int(n)
+        lo, hi = max(0, n - s_new), n
+        if hi > lo:
+            rows += hi - lo
+            pages += (hi - 1) // 64 - lo // 64 + 1
+    return 2 * 1152 * rows + 4 * pages + 4 * inp.batch
+
+
+def run_append(name: str, steps: int, warmup: int):
+    """One step = one mla_kv_append call on the workload's new rows. Each call
+    writes the same rows (idempotent), timed call by call with HIP events on
+    the launch stream."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+
+    inp = make_append_workload(name)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    kv = to_dev(inp.kv_bits)
+    new = to_dev(inp.new_bits)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seqlens).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        mla.kv_append(new, sl, bt, kv)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        mla.kv_append(new, sl, bt, kv)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        mla.kv_append(new, sl, bt, kv)
+        b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    nbytes = append_bytes(inp)
+    gbps = nbytes / (ms_step * 1e-3) / 1e9
+    kern_gbps = nbytes / (float(np.median(call_ms)) * 1e-3) / 1e9
+    cnt = counter_entry(name)
+    traffic = cnt.get("bytes_per_call") if cnt else None
+    w = APPEND_WORKLOADS[name]
+    return {
+        "metric": "paged latent-cache append: achieved HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; BF16 N(0,1) new rows, shuffled block table)",
+        "config": {"workload": f"{name}: batch {inp.batch}, {w['s_new']} new tokens per sequence, "
+                               f"final lengths U[{w['lengths'][2]},{w['lengths'][3]}], rows of 576 bf16, page 64",
+                   "batch": inp.batch, "s_new": inp.s_new, "seed": w["seed"]},
+        "append_call_us_median": round(float(np.median(call_ms)) * 1e3, 2),
+        "append_call_us_min": round(float(call_ms.min()) * 1e3, 2),
+        "append_call_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbps, 1), "peak": MI355X_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(kern_gbps / MI355X_HBM_GBPS, 4), "traffic": traffic},
+        "kernel_digest": kernel_digest("kv_append"),
+    }
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
@@ -230,7 +378,7 @@ def _counter_rows(run_dir: str):
     return rows
 
 
-def _per_dispatch_kib(run_dir: str, kernel_substr: str, counter: str):
+def _per_dispatch_mean(run_dir: str, kernel_substr: str, counter: str):
     vals = [float(r["Counter_Value"]) for r in _counter_rows(run_dir)
             if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter]
     if not vals:
@@ -245,15 +393,15 @@ def ingest_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
     `kernel`, scaled so that the 1 GiB copy reads and writes 1 GiB, and store
     them in profiles/hbm_traffic.json under the current kernel digest."""
     cal_bytes = 1 << 30
-    cf, _ = _per_dispatch_kib(cal_fetch_dir, "copyBuffer", "FETCH_SIZE")
-    cw, _ = _per_dispatch_kib(cal_write_dir, "copyBuffer", "WRITE_SIZE")
+    cf, _ = _per_dispatch_mean(cal_fetch_dir, "copyBuffer", "FETCH_SIZE")
+    cw, _ = _per_dispatch_mean(cal_write_dir, "copyBuffer", "WRITE_SIZE")
     fetch_scale = cal_bytes / (cf * 1024.0)
     write_scale = cal_bytes / (cw * 1024.0)
-    f, nf = _per_dispatch_kib(fetch_dir, kernel, "FETCH_SIZE")
-    wr, nw = _per_dispatch_kib(write_dir, kernel, "WRITE_SIZE")
+    f, nf = _per_dispatch_mean(fetch_dir, kernel, "FETCH_SIZE")
+    wr, nw = _per_dispatch_mean(write_dir, kernel, "WRITE_SIZE")
     entry = {
         "kernel": kernel,
-        "kernel_digest": kernel_digest(),
+        "kernel_digest": kernel_digest(_op_of(workload)),
         "fetch_kib_per_dispatch": round(f, 1), "dispatches_fetch": nf,
         "write_kib_per_dispatch": round(wr, 1), "dispatches_write": nw,
         "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
@@ -273,7 +421,24 @@ def ingest_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
     print(json.dumps({workload: entry}))
 
 
-def summarize_trace(trace_dir: str, command: str, bench_log: str = "") -> str:
+def ingest_mfma(workload: str, kernel: str, mfma_dir: str, command: str):
+    """Add the MFMA BF16 op count of one rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16
+    run (ops in units of 512 FLOPs, per dispatch of `kernel`) to the workload's
+    entry in profiles/hbm_traffic.json, taken on the same kernel sources."""
+    v, n = _per_dispatch_mean(mfma_dir, kernel, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    with open(COUNTERS_FILE) as fh:
+        doc = json.load(fh)
+    entry = doc.get("workloads", {}).get(workload)
+    if not entry or entry.get("kernel_digest") != kernel_digest(_op_of(workload)):
+        raise SystemExit(f"no byte-counter entry for {workload} on the current sources; ingest those first")
+    entry.update({"mfma_mops_bf16_per_call": int(round(v)), "dispatches_mfma": n, "mfma_command": command})
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(doc, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({workload: entry}))
+
+
+def summarize_trace(trace_dir: str, command: str, bench_log: str = "", op: str = "decode") -> str:
     """Text summary of a rocprofv3 --kernel-trace --stats run (kernel stats CSV),
     with the bench JSON line of the same run when its log is given."""
     import csv
@@ -283,7 +448,7 @@ def summarize_trace(trace_dir: str, command: str, bench_log: str = "") -> str:
         raise SystemExit(f"no *kernel_stats.csv under {trace_dir}")
     with open(files[0]) as fh:
         rows = list(csv.DictReader(fh))
-    out = [f"command: {command}", f"kernel sources digest: {kernel_digest()}", "",
+    out = [f"command: {command}", f"kernel sources digest: {kernel_digest(op)}", "",
            f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'share':>7s}"]
     for r in rows:
         name = r["Name"].replace("(anonymous namespace)::", "")[:58]
@@ -307,7 +472,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="one of %s, or 'all'" % ", ".join(WORKLOADS))
+                    help="one of %s, or 'all'; with --op kv_append one of %s or 'all'"
+                         % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
+    ap.add_argument("--op", default="decode", choices=("decode", "kv_append"),
+                    help="decode (the hot path; default) or the paged cache append")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -317,6 +485,11 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
                     help="rocprofv3 --pmc output dirs: write profiles/hbm_traffic.json for --workload "
                          "(no GPU needed)")
+    ap.add_argument("--ingest-mfma", metavar="MFMA_DIR",
+                    help="rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 output dir: add the MFMA op count "
+                         "to profiles/hbm_traffic.json for --workload (no GPU needed)")
+    ap.add_argument("--no-stream-context", action="store_true",
+                    help="skip the torch streaming-read / copy bandwidth context")
     ap.add_argument("--kernel", default="mla_decode_rows16_kernel",
                     help="kernel name substring for --ingest-counters")
     ap.add_argument("--command", default="", help="profiling command recorded by --ingest-counters")
@@ -325,10 +498,14 @@ def main():
     args = ap.parse_args()
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace[0], args.command,
-                                         args.summarize_trace[1] if len(args.summarize_trace) > 1 else ""))
+                                         args.summarize_trace[1] if len(args.summarize_trace) > 1 else "",
+                                         _op_of(args.workload)))
         return
     if args.ingest_counters:
         ingest_counters(args.workload, args.kernel, *args.ingest_counters, command=args.command)
+        return
+    if args.ingest_mfma:
+        ingest_mfma(args.workload, args.kernel, args.ingest_mfma, command=args.command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
@@ -337,11 +514,19 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.op == "kv_append":
+        names = list(APPEND_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]
+        for name in names:
+            print(json.dumps(run_append(name, args.steps, args.warmup)), flush=True)
+        return
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    ctx = None if args.no_stream_context else streaming_context()
     for name in names:
         line = run_workload(name, args.steps, args.warmup,
                             args.cpu_budget if name == DEFAULT_WORKLOAD or args.workload != "all" else 0,
                             int(args.rotate_gib * (1 << 30)), args.num_partitions)
+        if ctx:
+            line["achievable_context"] = ctx
         print(json.dumps(line), flush=True)
 
 

@@ -34,38 +34,49 @@ struct AppendArgs {
     int total_chunks;        // batch * s_new * 72
 };
 
-// Destination chunk index of source chunk g, or -1 when its token is not
-// written. Counts a token without a page once (at its first chunk).
-__device__ __forceinline__ long long append_target(const AppendArgs& a, int g) {
-    const int row = g / kRowChunks;
-    const int c = g - row * kRowChunks;
-    const int b = row / a.s_new;
-    const int i = row - b * a.s_new;
-    const int p = a.seqlens[b] - a.s_new + i;
-    if (p < 0) return -1;
-    const int blk = p >> 6;
-    int page = -1;
-    if (blk < a.max_blocks) page = a.block_table[(size_t)b * a.max_blocks + blk];
-    if (page < 0 || page >= a.num_pages) {
-        if (c == 0 && a.skipped) atomicAdd(a.skipped, 1);
-        return -1;
-    }
-    return ((long long)page * kPageRows + (p & (kPageRows - 1))) * kRowChunks + c;
-}
-
 __global__ __launch_bounds__(kAppendThreads) void mla_kv_append_kernel(AppendArgs a) {
     const int g0 = blockIdx.x * kAppendChunksPerBlock + threadIdx.x;
-    long long dst[kAppendUnroll];
-    u32x4 v[kAppendUnroll] = {};
+    const int last = a.total_chunks - 1;
+    // Three rounds over the thread's chunks: row loads, then the lengths,
+    // then the table entries, each round's loads all in flight together, so
+    // a wave waits for two memory latencies before its stores, not three per
+    // chunk. Every index is clamped into its buffer (a clamped chunk's result
+    // is discarded), so no load sits behind a branch.
+    u32x4 v[kAppendUnroll];
+    int g[kAppendUnroll], b[kAppendUnroll], p[kAppendUnroll], c[kAppendUnroll];
 #pragma unroll
     for (int u = 0; u < kAppendUnroll; ++u) {
-        const int g = g0 + u * kAppendThreads;
-        dst[u] = g < a.total_chunks ? append_target(a, g) : -1;
-        if (dst[u] >= 0) v[u] = __builtin_nontemporal_load(a.src + g);
+        g[u] = min(g0 + u * kAppendThreads, last);
+        v[u] = __builtin_nontemporal_load(a.src + g[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kAppendUnroll; ++u)
-        if (dst[u] >= 0) a.kv[dst[u]] = v[u];
+    for (int u = 0; u < kAppendUnroll; ++u) {
+        const int row = g[u] / kRowChunks;
+        c[u] = g[u] - row * kRowChunks;
+        b[u] = row / a.s_new;
+        p[u] = a.seqlens[b[u]] - a.s_new + (row - b[u] * a.s_new);   // position of the token
+    }
+    int blk[kAppendUnroll], page[kAppendUnroll];
+#pragma unroll
+    for (int u = 0; u < kAppendUnroll; ++u) {
+        blk[u] = max(p[u], 0) >> 6;
+        page[u] = a.block_table[(size_t)b[u] * a.max_blocks + min(blk[u], a.max_blocks - 1)];
+    }
+    // Pin the row data in registers here, before the stores' branches: left
+    // alone, the compiler moves each row load down into the branch of its
+    // store, where it is waited for on its own.
+#pragma unroll
+    for (int u = 0; u < kAppendUnroll; ++u) asm volatile("" : "+v"(v[u]));
+    int missing = 0;   // tokens of this thread with a position but no page
+#pragma unroll
+    for (int u = 0; u < kAppendUnroll; ++u) {
+        if (g0 + u * kAppendThreads > last) break;
+        const bool placed = p[u] >= 0;
+        const bool ok = placed & (blk[u] < a.max_blocks) & ((unsigned)page[u] < (unsigned)a.num_pages);
+        if (ok) a.kv[((long long)page[u] * kPageRows + (p[u] & (kPageRows - 1))) * kRowChunks + c[u]] = v[u];
+        missing += (placed & !ok & (c[u] == 0)) ? 1 : 0;
+    }
+    if (missing && a.skipped) atomicAdd(a.skipped, missing);
 }
 
 bool aligned_to(const void* p, size_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
