@@ -23,3 +23,4 @@ from .mla_ref import (  # noqa: F401
     mla_decode_bruteforce,
 )
 from .kv_append_ref import kv_append_ref  # noqa: F401
+from .absorb_ref import absorb_q_ref, absorb_o_ref  # noqa: F401

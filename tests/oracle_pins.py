@@ -266,3 +266,54 @@ def pin_append_round_trip(append, seed=31, s_new=9):
     out0, lse0 = oracle.mla_decode_ref(inp.q_bits, kv, inp.block_table, inp.seqlens, inp.scale, False)
     out1, lse1 = oracle.mla_decode_ref(inp.q_bits, restored, inp.block_table, inp.seqlens, inp.scale, False)
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# (m) Absorption, end to end: absorbing W_UK into the query, decoding over the
+# latent cache and applying W_UV afterwards equals the non-absorbed MLA form
+# (keys and values up-projected from the cache per head, then attention), for
+# several tokens with their own queries and head widths unlike 512.
+def pin_absorb_end_to_end(absorb_q, absorb_o, ref_f64, seed=32, n=130, heads=3, dn=96, dv=80):
+    rng = np.random.default_rng(seed)
+    c_kv = rng.standard_normal((n, 512))
+    k_rope = rng.standard_normal((n, 64))
+    w_uk = rng.standard_normal((heads, 512, dn)) / math.sqrt(512)
+    w_uv = rng.standard_normal((heads, 512, dv)) / math.sqrt(512)
+    tokens = 2
+    q_nope = rng.standard_normal((tokens, heads, dn))
+    q_rope = rng.standard_normal((tokens, heads, 64))
+    scale = 1.0 / math.sqrt(576)
+    q_abs = absorb_q(q_nope, q_rope, w_uk)                       # [T, H, 576]
+    kv, table = _paged(np.concatenate([c_kv, k_rope], axis=1), seed)
+    out_lat, _ = ref_f64(q_abs[None], kv, table, np.array([n]), scale, False)   # s_q = T
+    o = absorb_o(out_lat[0], w_uv)                               # [T, H, dv]
+    for t in range(tokens):
+        o_ref, _ = oracle.mla_nonabsorbed_ref(c_kv, k_rope, q_nope[t], q_rope[t], w_uk, w_uv, scale)
+        rel = np.abs(o[t] - o_ref).max() / np.abs(o_ref).max()
+        assert rel < 1e-12, f"token {t}: absorbed chain vs non-absorbed rel err {rel}"
+
+
+# (n) Selection weights: with W_UK_h placing q_nope coordinate d at latent
+# column sigma_h(d) (a 0/1 matrix) the absorbed query is q_nope scattered to
+# those columns, zero elsewhere, followed by q_rope; with W_UV_h picking
+# latent column tau_h(v) for output v the output gathers those columns.
+def pin_absorb_selection(absorb_q, absorb_o, seed=33, heads=3, dn=40, dv=24):
+    rng = np.random.default_rng(seed)
+    tokens = 5
+    q_nope = rng.standard_normal((tokens, heads, dn))
+    q_rope = rng.standard_normal((tokens, heads, 64))
+    o_lat = rng.standard_normal((tokens, heads, 512))
+    w_uk = np.zeros((heads, 512, dn))
+    w_uv = np.zeros((heads, 512, dv))
+    sig = [rng.choice(512, size=dn, replace=False) for _ in range(heads)]
+    tau = [rng.choice(512, size=dv, replace=False) for _ in range(heads)]
+    for h in range(heads):
+        w_uk[h, sig[h], np.arange(dn)] = 1.0
+        w_uv[h, tau[h], np.arange(dv)] = 1.0
+    q_abs = absorb_q(q_nope, q_rope, w_uk)
+    o = absorb_o(o_lat, w_uv)
+    for h in range(heads):
+        expect = np.zeros((tokens, 512))
+        expect[:, sig[h]] = q_nope[:, h, :]
+        assert np.array_equal(q_abs[:, h, :512], expect), f"head {h}: absorbed query"
+        assert np.array_equal(q_abs[:, h, 512:], q_rope[:, h, :]), f"head {h}: rotary part"
+        assert np.array_equal(o[:, h, :], o_lat[:, h, tau[h]]), f"head {h}: output"

@@ -194,3 +194,65 @@ def test_unmutated_append_passes_its_pins():
 @pytest.mark.parametrize("name", sorted(APPEND_MUTATIONS))
 def test_append_mutation_is_caught(name):
     assert _run_append_pins(APPEND_MUTATIONS[name]), f"append mutation {name} passed every pin"
+
+
+# ---- absorption ----------------------------------------------------------------
+
+def _absorb_q_variant(head_fn=None, rope_fn=None, scale=1.0):
+    def absorb_q(q_nope, q_rope, w_uk):
+        q_nope = np.asarray(q_nope, dtype=np.float64)
+        tokens, heads, dn = q_nope.shape
+        out = np.empty((tokens, heads, 576))
+        for h in range(heads):
+            w = w_uk[head_fn(h, heads) if head_fn else h]
+            out[:, h, :512] = scale * (q_nope[:, h, :] @ w.T)
+        out[:, :, 512:] = rope_fn(q_rope) if rope_fn else q_rope
+        return out
+    return absorb_q
+
+
+def _absorb_o_variant(head_fn=None, scale=1.0, token_shift=False):
+    def absorb_o(o_lat, w_uv):
+        o_lat = np.asarray(o_lat, dtype=np.float64)
+        tokens, heads, _ = o_lat.shape
+        out = np.empty((tokens, heads, w_uv.shape[-1]))
+        for h in range(heads):
+            out[:, h, :] = scale * (o_lat[:, h, :] @ w_uv[head_fn(h, heads) if head_fn else h])
+        if token_shift:
+            out = np.roll(out, 1, axis=0)
+        return out
+    return absorb_o
+
+
+ABSORB_MUTATIONS = {
+    "q_wrong_head": (_absorb_q_variant(head_fn=lambda h, n: (h + 1) % n), None),
+    "q_rope_dropped": (_absorb_q_variant(rope_fn=lambda r: np.zeros_like(r)), None),
+    "q_rope_other_head": (_absorb_q_variant(rope_fn=lambda r: np.roll(r, 1, axis=1)), None),
+    "q_extra_scale": (_absorb_q_variant(scale=1.0 / math.sqrt(128)), None),
+    "o_wrong_head": (None, _absorb_o_variant(head_fn=lambda h, n: (h + 1) % n)),
+    "o_extra_scale": (None, _absorb_o_variant(scale=0.5)),
+    "o_token_order": (None, _absorb_o_variant(token_shift=True)),
+}
+
+
+def _run_absorb_pins(aq, ao):
+    failed = []
+    pins = [("end_to_end", lambda: P.pin_absorb_end_to_end(aq, ao, R.mla_decode_ref_f64)),
+            ("selection", lambda: P.pin_absorb_selection(aq, ao))]
+    for name, fn in pins:
+        try:
+            fn()
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_absorb_passes_its_pins():
+    assert _run_absorb_pins(oracle.absorb_q_ref, oracle.absorb_o_ref) == []
+
+
+@pytest.mark.parametrize("name", sorted(ABSORB_MUTATIONS))
+def test_absorb_mutation_is_caught(name):
+    aq, ao = ABSORB_MUTATIONS[name]
+    assert _run_absorb_pins(aq or oracle.absorb_q_ref, ao or oracle.absorb_o_ref), \
+        f"absorb mutation {name} passed every pin"

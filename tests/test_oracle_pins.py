@@ -46,3 +46,11 @@ def test_append_physical_view():
 
 def test_append_round_trip():
     P.pin_append_round_trip(oracle.kv_append_ref)
+
+
+def test_absorb_end_to_end():
+    P.pin_absorb_end_to_end(oracle.absorb_q_ref, oracle.absorb_o_ref, oracle.mla_decode_ref_f64)
+
+
+def test_absorb_selection():
+    P.pin_absorb_selection(oracle.absorb_q_ref, oracle.absorb_o_ref)
