@@ -27,7 +27,7 @@ HEAD_DIM = 576
 HEAD_DIM_V = 512
 PAGE_SIZE = 64
 
-__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "kv_append", "split_metadata_host",
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "kv_append", "absorb_q", "absorb_o", "split_metadata_host",
            "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
 
 
@@ -200,6 +200,60 @@ def kv_append(new_rows: torch.Tensor, seqlens: torch.Tensor, block_table: torch.
                               skipped.data_ptr() if skipped is not None else None, _stream_ptr(dev)),
           "mla_kv_append")
     return kv_cache
+
+
+def absorb_q(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Absorbed decode query (mla_absorb_q): [W_UK_h q_nope ; q_rope] per token
+    and head. q_nope [..., h, d_nope], q_rope [..., h, 64] bf16 with the same
+    leading dims (e.g. [B, s_q]); w_uk [h, 512, d_nope] bf16. Returns
+    [..., h, 576] bf16, the q layout decode_fwd takes."""
+    dev = q_nope.device
+    _require(q_nope, "q_nope", torch.bfloat16)
+    _require(q_rope, "q_rope", torch.bfloat16, device=dev)
+    _require(w_uk, "w_uk", torch.bfloat16, device=dev, ndim=3)
+    if q_nope.dim() < 2 or q_rope.shape[:-1] != q_nope.shape[:-1] or q_rope.shape[-1] != 64:
+        raise ValueError("q_rope must be [..., h, 64] with q_nope's leading dims")
+    h, d_nope = q_nope.shape[-2], q_nope.shape[-1]
+    if tuple(w_uk.shape) != (h, HEAD_DIM_V, d_nope):
+        raise ValueError(f"w_uk must be [{h}, 512, {d_nope}], got {tuple(w_uk.shape)}")
+    tokens = q_nope.numel() // (h * d_nope)
+    shape = (*q_nope.shape[:-1], HEAD_DIM)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    else:
+        _require(out, "out", torch.bfloat16, device=dev)
+        if tuple(out.shape) != shape:
+            raise ValueError("out has the wrong shape")
+    check(lib().mla_absorb_q(q_nope.data_ptr(), q_rope.data_ptr(), w_uk.data_ptr(), tokens, h, d_nope,
+                             out.data_ptr(), _stream_ptr(dev)), "mla_absorb_q")
+    return out
+
+
+def absorb_o(o_lat: torch.Tensor, w_uv_t: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Head outputs from the latent decode output (mla_absorb_o): o_lat W_UV_h
+    per token and head. o_lat [..., h, 512] bf16 (decode_fwd's out); w_uv_t
+    [h, d_v, 512] bf16, W_UV_h transposed per head. Returns [..., h, d_v] bf16."""
+    dev = o_lat.device
+    _require(o_lat, "o_lat", torch.bfloat16)
+    _require(w_uv_t, "w_uv_t", torch.bfloat16, device=dev, ndim=3)
+    if o_lat.dim() < 2 or o_lat.shape[-1] != HEAD_DIM_V:
+        raise ValueError("o_lat must be [..., h, 512]")
+    h = o_lat.shape[-2]
+    if w_uv_t.shape[0] != h or w_uv_t.shape[2] != HEAD_DIM_V:
+        raise ValueError(f"w_uv_t must be [{h}, d_v, 512], got {tuple(w_uv_t.shape)}")
+    d_v = w_uv_t.shape[1]
+    tokens = o_lat.numel() // (h * HEAD_DIM_V)
+    shape = (*o_lat.shape[:-1], d_v)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    else:
+        _require(out, "out", torch.bfloat16, device=dev)
+        if tuple(out.shape) != shape:
+            raise ValueError("out has the wrong shape")
+    check(lib().mla_absorb_o(o_lat.data_ptr(), w_uv_t.data_ptr(), tokens, h, d_v, out.data_ptr(),
+                             _stream_ptr(dev)), "mla_absorb_o")
+    return out
 
 
 def timing_enable(enable: bool = True) -> None:

@@ -134,3 +134,38 @@ def _append(**kw):
 ])
 def test_append_argument_checks(kw, status):
     assert _append(**kw) == status
+
+
+def _absorb_q(**kw):
+    args = dict(qn=FAKE, qr=FAKE, w=FAKE, tokens=4, h=2, dn=128, out=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_absorb_q(args["qn"], args["qr"], args["w"], args["tokens"], args["h"], args["dn"],
+                                   args["out"], args["stream"])
+
+
+def _absorb_o(**kw):
+    args = dict(o=FAKE, w=FAKE, tokens=4, h=2, dv=128, out=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_absorb_o(args["o"], args["w"], args["tokens"], args["h"], args["dv"], args["out"],
+                                   args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qn=None), INVALID), (dict(qr=None), INVALID), (dict(w=None), INVALID), (dict(out=None), INVALID),
+    (dict(tokens=0), INVALID), (dict(h=0), INVALID), (dict(dn=16), INVALID), (dict(dn=100), INVALID),
+    (dict(dn=544), INVALID), (dict(tokens=1 << 20, h=4096), UNSUPPORTED),
+    (dict(qn=FAKE + 2), MISALIGNED), (dict(qr=FAKE + 8), MISALIGNED), (dict(w=FAKE + 4), MISALIGNED),
+    (dict(out=FAKE + 8), MISALIGNED),
+])
+def test_absorb_q_argument_checks(kw, status):
+    assert _absorb_q(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), INVALID), (dict(w=None), INVALID), (dict(out=None), INVALID), (dict(tokens=0), INVALID),
+    (dict(h=0), INVALID), (dict(dv=0), INVALID), (dict(dv=48), INVALID), (dict(dv=1024), INVALID),
+    (dict(tokens=1 << 20, h=4096), UNSUPPORTED),
+    (dict(o=FAKE + 8), MISALIGNED), (dict(w=FAKE + 2), MISALIGNED), (dict(out=FAKE + 4), MISALIGNED),
+])
+def test_absorb_o_argument_checks(kw, status):
+    assert _absorb_o(**kw) == status
