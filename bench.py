@@ -26,8 +26,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (APPEND_WORKLOADS, MI355X_BF16_TFLOPS, MI355X_HBM_GBPS, WORKLOADS,  # noqa: E402
-                       algorithmic_bytes, algorithmic_flops, make_append_workload, make_workload_inputs)
+from workloads import (ABSORB_WORKLOADS, APPEND_WORKLOADS, MI355X_BF16_TFLOPS, MI355X_HBM_GBPS,  # noqa: E402
+                       WORKLOADS, algorithmic_bytes, algorithmic_flops, make_absorb_workload,
+                       make_append_workload, make_workload_inputs)
 
 METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
 DEFAULT_WORKLOAD = "memory_bound"
@@ -35,20 +36,22 @@ CSRC = os.path.join(ROOT, "mla_paged_kv_02_amd", "csrc")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-# Sources of the cache-append op; the decode path's digest leaves them out,
-# so that changing one does not void the other's counter figures.
-APPEND_SOURCES = ("mla_kv_append.hip", "mla_common.h")
+# Sources of the ops beside decode; the decode path's digest leaves their
+# kernels out, so that changing one op does not void another's counter figures.
+OP_SOURCES = {"kv_append": ("mla_kv_append.hip", "mla_common.h"),
+              "absorb": ("mla_absorb.hip", "mla_common.h")}
 
 
 def kernel_digest(op: str = "decode") -> str:
-    """Digest of the library sources an op's kernels are built from: every
-    source but the append kernel for decode, the append kernel and the shared
-    constants for kv_append."""
+    """Digest of the library sources an op's kernels are built from: for
+    decode every source but the other ops' kernels, for another op its kernel
+    file and the shared helpers."""
+    own_files = {srcs[0] for srcs in OP_SOURCES.values()}
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if op == "kv_append" and f not in APPEND_SOURCES:
+        if op != "decode" and f not in OP_SOURCES[op]:
             continue
-        if op == "decode" and f == APPEND_SOURCES[0]:
+        if op == "decode" and f in own_files:
             continue
         if f.endswith((".hip", ".h", ".cpp")):
             h.update(f.encode())
@@ -73,7 +76,11 @@ def counter_entry(workload: str):
 
 
 def _op_of(workload: str) -> str:
-    return "kv_append" if workload in APPEND_WORKLOADS else "decode"
+    if workload in APPEND_WORKLOADS:
+        return "kv_append"
+    if workload in ABSORB_WORKLOADS:
+        return "absorb"
+    return "decode"
 
 
 def cpu_model() -> str:
@@ -351,6 +358,99 @@ def run_append(name: str, steps: int, warmup: int):
     }
 
 
+def absorb_work(w: dict):
+    """Algorithmic bytes and FLOPs of absorb_q and absorb_o: every operand
+    read once and every result written once; 2 FLOPs per multiply-add."""
+    t, h, dn, dv = w["tokens"], w["heads"], w["d_nope"], w["d_v"]
+    q_bytes = 2 * (t * h * dn + t * h * 64 + h * 512 * dn + t * h * 576)
+    o_bytes = 2 * (t * h * 512 + h * 512 * dv + t * h * dv)
+    return q_bytes, 2 * t * h * 512 * dn, o_bytes, 2 * t * h * 512 * dv
+
+
+def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
+    """One step = mla_absorb_q then mla_absorb_o for one decode step's tokens.
+    Inputs and weights are replicated so consecutive steps read different
+    copies (>= rotate_bytes in rotation, so weights do not stay in the MALL);
+    each kernel is also timed call by call with HIP events on its stream."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+
+    w = ABSORB_WORKLOADS[name]
+    inp = make_absorb_workload(name)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = [to_dev(inp.q_nope), to_dev(inp.q_rope), to_dev(inp.w_uk), to_dev(inp.o_lat),
+            to_dev(np.ascontiguousarray(inp.w_uv.transpose(0, 2, 1)))]
+    set_bytes = sum(t.numel() * 2 for t in base)
+    copies = max(1, min(32, math.ceil(rotate_bytes / set_bytes)))
+    sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+    q_abs = torch.empty((w["tokens"], w["heads"], 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w["tokens"], w["heads"], w["d_v"]), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        qn, qr, wuk, ol, wuv = sets[i % copies]
+        if ev:
+            ev[0].record(stream)
+        mla.absorb_q(qn, qr, wuk, out=q_abs)
+        if ev:
+            ev[1].record(stream)
+        mla.absorb_o(ol, wuv, out=out)
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    o_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    qb, qf, ob, of = absorb_work(w)
+    q_gbps = qb / (float(np.median(q_ms)) * 1e-3) / 1e9
+    o_gbps = ob / (float(np.median(o_ms)) * 1e-3) / 1e9
+    cnt = counter_entry(name)
+
+    def roof(gbps, key):
+        return {"bound": "hbm", "achieved": round(gbps, 1), "peak": MI355X_HBM_GBPS, "unit": "GB/s",
+                "frac": round(gbps / MI355X_HBM_GBPS, 4),
+                "traffic": (cnt or {}).get(key)}
+
+    return {
+        "metric": "MLA absorption products (absorb_q + absorb_o): achieved HBM GB/s",
+        "value": round((qb + ob) / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; BF16 N(0,1) activations, N(0,1/K) weights)",
+        "config": {"workload": f"{name}: {w['tokens']} tokens, {w['heads']} heads, d_nope {w['d_nope']}, "
+                               f"d_v {w['d_v']}, latent 512", **{k: w[k] for k in ("tokens", "heads", "d_nope", "d_v")}},
+        "tflops": round((qf + of) / (ms_step * 1e-3) / 1e12, 2),
+        "absorb_q_us_median": round(float(np.median(q_ms)) * 1e3, 2),
+        "absorb_q_us_p90": round(float(np.percentile(q_ms, 90)) * 1e3, 2),
+        "absorb_o_us_median": round(float(np.median(o_ms)) * 1e3, 2),
+        "absorb_o_us_p90": round(float(np.percentile(o_ms, 90)) * 1e3, 2),
+        "algorithmic_bytes": {"absorb_q": qb, "absorb_o": ob},
+        "algorithmic_flops": {"absorb_q": qf, "absorb_o": of},
+        "copies_rotated": copies,
+        "roofline": roof(q_gbps, "bytes_per_call"),
+        "roofline_absorb_o": roof(o_gbps, "absorb_o_bytes_per_call"),
+        "kernel_digest": kernel_digest("absorb"),
+    }
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, to calibrate the HBM
     byte counters (FETCH_SIZE / WRITE_SIZE) read by rocprofv3."""
@@ -474,8 +574,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="one of %s, or 'all'; with --op kv_append one of %s or 'all'"
                          % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
-    ap.add_argument("--op", default="decode", choices=("decode", "kv_append"),
-                    help="decode (the hot path; default) or the paged cache append")
+    ap.add_argument("--op", default="decode", choices=("decode", "kv_append", "absorb"),
+                    help="decode (the hot path; default), the paged cache append, or the absorption "
+                         "products")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -513,6 +614,12 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "absorb":
+        names = list(ABSORB_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]
+        for name in names:
+            print(json.dumps(run_absorb(name, args.steps, args.warmup, int(args.rotate_gib * (1 << 30)))),
+                  flush=True)
         return
     if args.op == "kv_append":
         names = list(APPEND_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]

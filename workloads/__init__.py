@@ -25,6 +25,10 @@ from .gen import (  # noqa: F401
     APPEND_WORKLOADS,
     make_append_inputs,
     make_append_workload,
+    ABSORB_WORKLOADS,
+    AbsorbInputs,
+    make_absorb_inputs,
+    make_absorb_workload,
 )
 from .roofline import (  # noqa: F401
     algorithmic_bytes,

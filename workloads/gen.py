@@ -257,3 +257,41 @@ def make_append_workload(name: str) -> AppendInputs:
     base = make_inputs(seqlens, 1, 1, w["seed"], rng=rng)
     new_bits = _standard_normal_bf16(rng, (n, w["s_new"], HEAD_DIM))
     return AppendInputs(base.seqlens, base.block_table, base.kv_bits, new_bits)
+
+
+# Absorption workloads: the query and output projections around one decode
+# step of the 128-head workloads (d_nope = d_v = 128, as in the 128-head MLA
+# models these shapes come from). Weights are N(0, 1/K) so outputs keep unit
+# scale.
+ABSORB_WORKLOADS = {
+    "absorb_compute_leaning": dict(tokens=128, heads=128, d_nope=128, d_v=128, seed=23),
+    "absorb_multi_token": dict(tokens=264, heads=128, d_nope=128, d_v=128, seed=24),
+}
+
+
+@dataclasses.dataclass
+class AbsorbInputs:
+    q_nope: np.ndarray     # uint16 [T, H, d_nope]
+    q_rope: np.ndarray     # uint16 [T, H, 64]
+    w_uk: np.ndarray       # uint16 [H, 512, d_nope]
+    o_lat: np.ndarray      # uint16 [T, H, 512]
+    w_uv: np.ndarray       # uint16 [H, 512, d_v]
+
+
+def make_absorb_inputs(tokens: int, heads: int, d_nope: int, d_v: int, seed: int) -> AbsorbInputs:
+    rng = np.random.default_rng(seed)
+
+    def draw(shape, std=1.0):
+        return bf16_round_bits((rng.standard_normal(shape, dtype=np.float32) * np.float32(std)))
+
+    q_nope = draw((tokens, heads, d_nope))
+    q_rope = draw((tokens, heads, 64))
+    w_uk = draw((heads, 512, d_nope), 1.0 / math.sqrt(d_nope))
+    o_lat = draw((tokens, heads, 512))
+    w_uv = draw((heads, 512, d_v), 1.0 / math.sqrt(512))
+    return AbsorbInputs(q_nope, q_rope, w_uk, o_lat, w_uv)
+
+
+def make_absorb_workload(name: str) -> AbsorbInputs:
+    w = ABSORB_WORKLOADS[name]
+    return make_absorb_inputs(w["tokens"], w["heads"], w["d_nope"], w["d_v"], w["seed"])
