@@ -282,6 +282,26 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     return line
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_queue(ms: float):
+    """Enqueue a device-side spin of about `ms` on the current stream, so that
+    the calls that follow are all queued before the GPU reaches them. The
+    events around them then time device work only: these ops run for a few
+    microseconds, less than one Python-side launch takes on the host."""
+    import torch
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:   # calibrate the spin's counter rate once
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
 def append_bytes(inp) -> int:
     """Algorithmic bytes of one cache append: each placed token's row read once
     and written once (2 x 1152 B), one block-table entry per (sequence, page)
@@ -300,7 +320,8 @@ def append_bytes(inp) -> int:
 def run_append(name: str, steps: int, warmup: int):
     """One step = one mla_kv_append call on the workload's new rows. Each call
     writes the same rows (idempotent), timed call by call with HIP events on
-    the launch stream."""
+    the launch stream, behind a device-side spin that keeps the host's launch
+    cost out of the events."""
     import torch
     import mla_paged_kv_02_amd as mla
 
@@ -320,6 +341,7 @@ def run_append(name: str, steps: int, warmup: int):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    hold_queue(0.1 * steps)
     t0.record(stream)
     for _ in range(steps):
         mla.kv_append(new, sl, bt, kv)
@@ -327,6 +349,7 @@ def run_append(name: str, steps: int, warmup: int):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    hold_queue(0.1 * steps)
     for a, b in evs:
         a.record(stream)
         mla.kv_append(new, sl, bt, kv)
@@ -335,7 +358,10 @@ def run_append(name: str, steps: int, warmup: int):
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
     nbytes = append_bytes(inp)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
-    kern_gbps = nbytes / (float(np.median(call_ms)) * 1e-3) / 1e9
+    # the kernel's duration for the roofline: the back-to-back average (an
+    # event pair around every call adds a few microseconds of its own, which
+    # is most of a one-decode-step append)
+    kern_gbps = gbps
     cnt = counter_entry(name)
     traffic = cnt.get("bytes_per_call") if cnt else None
     w = APPEND_WORKLOADS[name]
@@ -348,6 +374,7 @@ def run_append(name: str, steps: int, warmup: int):
         "config": {"workload": f"{name}: batch {inp.batch}, {w['s_new']} new tokens per sequence, "
                                f"final lengths U[{w['lengths'][2]},{w['lengths'][3]}], rows of 576 bf16, page 64",
                    "batch": inp.batch, "s_new": inp.s_new, "seed": w["seed"]},
+        "append_kernel_us_avg": round(ms_step * 1e3, 2),
         "append_call_us_median": round(float(np.median(call_ms)) * 1e3, 2),
         "append_call_us_min": round(float(call_ms.min()) * 1e3, 2),
         "append_call_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2),
@@ -371,7 +398,9 @@ def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
     """One step = mla_absorb_q then mla_absorb_o for one decode step's tokens.
     Inputs and weights are replicated so consecutive steps read different
     copies (>= rotate_bytes in rotation, so weights do not stay in the MALL);
-    each kernel is also timed call by call with HIP events on its stream."""
+    each kernel is also timed call by call with HIP events on its stream.
+    Both timed passes start behind a device-side spin that keeps the host's
+    launch cost out of the events."""
     import torch
     import mla_paged_kv_02_amd as mla
 
@@ -407,6 +436,7 @@ def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    hold_queue(0.2 * steps)
     t0.record(stream)
     for i in range(steps):
         step(i)
@@ -414,14 +444,31 @@ def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    hold_queue(0.2 * steps)
     for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     q_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     o_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+
+    def batch_avg_ms(call):
+        # one kernel back to back over the rotated copies, one event pair
+        # around the batch: its average duration for the roofline (an event
+        # pair around every call adds a few microseconds of its own)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        hold_queue(0.1 * steps)
+        a.record(stream)
+        for i in range(steps):
+            call(sets[i % copies])
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    q_avg = batch_avg_ms(lambda st: mla.absorb_q(st[0], st[1], st[2], out=q_abs))
+    o_avg = batch_avg_ms(lambda st: mla.absorb_o(st[3], st[4], out=out))
     qb, qf, ob, of = absorb_work(w)
-    q_gbps = qb / (float(np.median(q_ms)) * 1e-3) / 1e9
-    o_gbps = ob / (float(np.median(o_ms)) * 1e-3) / 1e9
+    q_gbps = qb / (q_avg * 1e-3) / 1e9
+    o_gbps = ob / (o_avg * 1e-3) / 1e9
     cnt = counter_entry(name)
 
     def roof(gbps, key):
@@ -438,6 +485,8 @@ def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
         "config": {"workload": f"{name}: {w['tokens']} tokens, {w['heads']} heads, d_nope {w['d_nope']}, "
                                f"d_v {w['d_v']}, latent 512", **{k: w[k] for k in ("tokens", "heads", "d_nope", "d_v")}},
         "tflops": round((qf + of) / (ms_step * 1e-3) / 1e12, 2),
+        "absorb_q_kernel_us_avg": round(q_avg * 1e3, 2),
+        "absorb_o_kernel_us_avg": round(o_avg * 1e3, 2),
         "absorb_q_us_median": round(float(np.median(q_ms)) * 1e3, 2),
         "absorb_q_us_p90": round(float(np.percentile(q_ms, 90)) * 1e3, 2),
         "absorb_o_us_median": round(float(np.median(o_ms)) * 1e3, 2),
@@ -487,11 +536,13 @@ def _per_dispatch_mean(run_dir: str, kernel_substr: str, counter: str):
 
 
 def ingest_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
-                    cal_fetch_dir: str, cal_write_dir: str, command: str):
+                    cal_fetch_dir: str, cal_write_dir: str, command: str, key: str = ""):
     """Turn four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench on
     `workload`, and of --copy-calibration) into HBM bytes per dispatch of
     `kernel`, scaled so that the 1 GiB copy reads and writes 1 GiB, and store
-    them in profiles/hbm_traffic.json under the current kernel digest."""
+    them in profiles/hbm_traffic.json under the current kernel digest. With
+    `key`, the figures of a second kernel of the same workload are added to
+    its entry as `<key>` and `<key>_bytes_per_call`."""
     cal_bytes = 1 << 30
     cf, _ = _per_dispatch_mean(cal_fetch_dir, "copyBuffer", "FETCH_SIZE")
     cw, _ = _per_dispatch_mean(cal_write_dir, "copyBuffer", "WRITE_SIZE")
@@ -514,6 +565,13 @@ def ingest_counters(workload: str, kernel: str, fetch_dir: str, write_dir: str,
             doc = json.load(fh)
     except (OSError, ValueError):
         doc = {}
+    if key:
+        main = doc.get("workloads", {}).get(workload)
+        if not main or main.get("kernel_digest") != entry["kernel_digest"]:
+            raise SystemExit(f"no entry for {workload} on the current sources; ingest its first kernel first")
+        main[key] = entry
+        main[key + "_bytes_per_call"] = entry["bytes_per_call"]
+        entry = main
     doc.setdefault("workloads", {})[workload] = entry
     with open(COUNTERS_FILE, "w") as fh:
         json.dump(doc, fh, indent=1, sort_keys=True)
@@ -594,6 +652,9 @@ def main():
     ap.add_argument("--kernel", default="mla_decode_rows16_kernel",
                     help="kernel name substring for --ingest-counters")
     ap.add_argument("--command", default="", help="profiling command recorded by --ingest-counters")
+    ap.add_argument("--counter-key", default="",
+                    help="with --ingest-counters: add a second kernel's bytes to the workload's entry "
+                         "under this key")
     ap.add_argument("--summarize-trace", nargs="+", metavar=("TRACE_DIR", "BENCH_LOG"),
                     help="print a text summary of a rocprofv3 --kernel-trace --stats run (no GPU)")
     args = ap.parse_args()
@@ -603,7 +664,8 @@ def main():
                                          _op_of(args.workload)))
         return
     if args.ingest_counters:
-        ingest_counters(args.workload, args.kernel, *args.ingest_counters, command=args.command)
+        ingest_counters(args.workload, args.kernel, *args.ingest_counters, command=args.command,
+                        key=args.counter_key)
         return
     if args.ingest_mfma:
         ingest_mfma(args.workload, args.kernel, args.ingest_mfma, command=args.command)

@@ -58,7 +58,10 @@ int kernel_override() {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Benchmark timing: three events per recorded call (before decode, between
-// decode and combine, after combine), pooled and reused.
+// decode and combine, after combine), pooled and reused. They are created
+// without the system-scope fence a default event performs when it completes
+// (an L2 writeback and invalidate): they only time work, and that fence
+// would add microseconds to every kernel they bracket.
 struct CallEvents {
     hipEvent_t ev[3];
 };
@@ -78,7 +81,7 @@ CallEvents* timing_slot() {
     if (g_timing.used == g_timing.pool.size()) {
         CallEvents ce{};
         for (int i = 0; i < 3; ++i) {
-            if (hipEventCreate(&ce.ev[i]) != hipSuccess) {
+            if (hipEventCreateWithFlags(&ce.ev[i], hipEventDisableSystemFence) != hipSuccess) {
                 (void)hipGetLastError();
                 for (int j = 0; j < i; ++j) (void)hipEventDestroy(ce.ev[j]);
                 return nullptr;
