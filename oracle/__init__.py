@@ -24,3 +24,10 @@ from .mla_ref import (  # noqa: F401
 )
 from .kv_append_ref import kv_append_ref  # noqa: F401
 from .absorb_ref import absorb_q_ref, absorb_o_ref  # noqa: F401
+from .fp8_ref import (  # noqa: F401
+    e4m3_value,
+    e4m3_decode,
+    quantize_e4m3_rows,
+    dequantize_fp8_cache,
+    mla_decode_fp8_ref,
+)

@@ -317,3 +317,76 @@ def pin_absorb_selection(absorb_q, absorb_o, seed=33, heads=3, dn=40, dv=24):
         assert np.array_equal(q_abs[:, h, :512], expect), f"head {h}: absorbed query"
         assert np.array_equal(q_abs[:, h, 512:], q_rope[:, h, :]), f"head {h}: rotary part"
         assert np.array_equal(o[:, h, :], o_lat[:, h, tau[h]]), f"head {h}: output"
+
+
+# (o) E4M3 values fixed by the OCP 8-bit floating point specification: zero
+# and negative zero, the smallest subnormal 2^-9, the largest subnormal
+# 7 * 2^-9, the smallest normal 2^-6, one, one and a half, the largest
+# normal 448, NaN only at S.1111.111, and 254 finite values increasing with
+# the code within each sign.
+def pin_e4m3_table(decode):
+    v = decode(np.arange(256, dtype=np.uint8))
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+             0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for code, val in fixed.items():
+        assert v[code] == val, f"E4M3 0x{code:02x} = {v[code]}, expected {val}"
+    assert v[0x80] == 0.0 and math.copysign(1.0, v[0x80]) < 0, "0x80 must be -0"
+    nan = np.isnan(v)
+    assert set(np.flatnonzero(nan)) == {0x7F, 0xFF}, "NaN codes"
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0), "positive codes not increasing"
+    assert np.array_equal(v[0x80:0xFF], -pos), "negative codes are not the mirror"
+
+
+# (p) Quantiser: the largest magnitude of a row lands on +-448 exactly; a row
+# made of E4M3 values times a power of two comes back bit for bit; every
+# value is within half a step of the grid at its magnitude; and an exact
+# midpoint between two neighbours rounds to the even mantissa.
+def pin_e4m3_quantizer(quantize, decode, seed=34):
+    rng = np.random.default_rng(seed)
+    rows = rng.standard_normal((6, 512)) * np.array([1e-3, 0.5, 1.0, 3.0, 100.0, 1e4])[:, None]
+    codes, scale = quantize(rows)
+    back = decode(codes) * scale.astype(np.float64)[:, None]
+    for r in range(rows.shape[0]):
+        k = np.argmax(np.abs(rows[r]))
+        assert abs(decode(codes[r, k:k + 1])[0]) == 448.0, "row maximum must map to 448"
+        y = rows[r] / float(scale[r])
+        # grid step at |y|: 2^(e-3) for normals (e = floor(log2|y|)), 2^-9 below 2^-6
+        e = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6)))
+        step = 2.0 ** (e - 3)
+        err = np.abs(back[r] / float(scale[r]) - y)
+        assert np.all(err <= step / 2 * (1 + 1e-12)), "quantisation error above half a step"
+    exact = decode(rng.integers(0, 0x7F, size=(3, 512)).astype(np.uint8))
+    exact[:, 0] = 448.0                    # fixes amax, so scale = 2^k exactly
+    exact *= 2.0 ** np.array([-3, 0, 5])[:, None]
+    c2, s2 = quantize(exact)
+    assert np.array_equal(decode(c2) * s2.astype(np.float64)[:, None], exact), "exact values not kept"
+    # midpoints: 1 + 1/16 lies between 1 (even mantissa 0) and 1.125 (odd);
+    # 1.125 + 1/16 between 1.125 (odd) and 1.25 (even)
+    row = np.zeros((1, 512))
+    row[0, 0] = 448.0
+    row[0, 1], row[0, 2] = 1.0625, 1.1875
+    c3, s3 = quantize(row)
+    assert float(s3[0]) == 1.0
+    assert decode(c3[0, 1:3]).tolist() == [1.0, 1.25], "ties must go to the even mantissa"
+
+
+# (q) FP8 decode against the BF16 path: when every latent value is exactly
+# an E4M3 value times a power-of-two scale (so also exactly a BF16 value),
+# decode over the FP8 cache equals the BF16 reference over the same rows
+# written as BF16, bit for bit.
+def pin_fp8_decode_matches_bf16(decode_fp8, ref_bits, seed=35):
+    from workloads import bf16_round_bits
+    rng = np.random.default_rng(seed)
+    inp = make_inputs([70, 5, 129], s_q=2, h_q=4, seed=seed, causal=True)
+    pages = inp.kv_bits.shape[0]
+    codes = rng.integers(0, 0x7F, size=(pages, 64, 512)).astype(np.uint8)
+    codes[rng.random(codes.shape) < 0.5] |= 0x80                     # both signs
+    scales = (2.0 ** rng.integers(-8, -3, size=(pages, 64))).astype(np.float32)
+    rope = inp.kv_bits[:, :, 0, 512:]
+    lat = oracle.e4m3_decode(codes) * scales.astype(np.float64)[..., None]
+    kv_bits = np.concatenate([bf16_round_bits(lat.astype(np.float32)), rope], axis=-1)[:, :, None, :]
+    assert np.array_equal(_f64(kv_bits[..., :512])[:, :, 0], lat), "test rows not exact in BF16"
+    o1, l1 = decode_fp8(inp.q_bits, codes, rope, scales, inp.block_table, inp.seqlens, inp.scale, True)
+    o2, l2 = ref_bits(inp.q_bits, kv_bits, inp.block_table, inp.seqlens, inp.scale, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "FP8 decode differs from BF16 decode"

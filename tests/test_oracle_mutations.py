@@ -256,3 +256,87 @@ def test_absorb_mutation_is_caught(name):
     aq, ao = ABSORB_MUTATIONS[name]
     assert _run_absorb_pins(aq or oracle.absorb_q_ref, ao or oracle.absorb_o_ref), \
         f"absorb mutation {name} passed every pin"
+
+
+# ---- FP8 cache -------------------------------------------------------------------
+
+def _e4m3_variant(bias=7, subnormal_implicit=False, ignore_sign=False):
+    def value(byte):
+        sign = 1.0 if (ignore_sign or not byte & 0x80) else -1.0
+        exp, man = (byte >> 3) & 0xF, byte & 0x7
+        if exp == 0xF and man == 0x7:
+            return math.nan
+        if exp == 0 and not subnormal_implicit:
+            return sign * (man / 8.0) * 2.0 ** (1 - bias)
+        return sign * (1.0 + man / 8.0) * 2.0 ** (exp - bias)
+    table = np.array([value(b) for b in range(256)])
+    return lambda codes: table[np.asarray(codes, dtype=np.uint8)]
+
+
+def _quantize_variant(ties_away=False, limit=448.0):
+    def quantize(rows):
+        rows = np.asarray(rows, dtype=np.float64)
+        amax = np.abs(rows).max(axis=1)
+        scale = np.where(amax > 0, amax / limit, 1.0).astype(np.float32)
+        y = rows / scale.astype(np.float64)[:, None]
+        codes = np.array([b for b in range(256) if not math.isnan(oracle.e4m3_value(b)) and b != 0x80])
+        vals = np.array([oracle.e4m3_value(b) for b in codes])
+        out = np.empty(y.shape, dtype=np.uint8)
+        for idx, x in np.ndenumerate(y):
+            d = np.abs(vals - x)
+            best = np.flatnonzero(d == d.min())
+            if len(best) > 1:
+                best = [max(best, key=lambda k: abs(vals[k]))] if ties_away else \
+                       [k for k in best if codes[k] & 1 == 0][:1]
+            out[idx] = codes[best[0]]
+        return out, scale
+    return quantize
+
+
+def _decode_fp8_variant(rope_scaled=False, scale_ignored=False):
+    def decode(q_bits, codes, rope_bits, scales, table, seqlens, scale, causal, seqs=None):
+        q = (np.asarray(q_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        s = np.ones_like(scales, dtype=np.float64) if scale_ignored else scales.astype(np.float64)
+        lat = oracle.e4m3_decode(codes) * s[..., None]
+        rope = (np.asarray(rope_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+        rope = rope.astype(np.float64) * (s[..., None] if rope_scaled else 1.0)
+        kv = np.concatenate([lat, rope], axis=-1)[:, :, None, :]
+        return R.mla_decode_ref_f64(q.astype(np.float64), kv, table, seqlens, float(np.float32(scale)), causal, seqs)
+    return decode
+
+
+def _run_fp8_pins(decode=None, quantize=None, fp8_decode=None):
+    decode = decode or oracle.e4m3_decode
+    quantize = quantize or oracle.quantize_e4m3_rows
+    fp8_decode = fp8_decode or oracle.mla_decode_fp8_ref
+    failed = []
+    pins = [("table", lambda: P.pin_e4m3_table(decode)),
+            ("quantizer", lambda: P.pin_e4m3_quantizer(quantize, decode)),
+            ("fp8_vs_bf16", lambda: P.pin_fp8_decode_matches_bf16(fp8_decode, R.mla_decode_ref))]
+    with np.errstate(all="ignore"):
+        for name, fn in pins:
+            try:
+                fn()
+            except Exception:  # noqa: BLE001 - any failure counts as caught
+                failed.append(name)
+    return failed
+
+
+FP8_MUTATIONS = {
+    "bias_8": dict(decode=_e4m3_variant(bias=8)),
+    "subnormal_as_normal": dict(decode=_e4m3_variant(subnormal_implicit=True)),
+    "sign_ignored": dict(decode=_e4m3_variant(ignore_sign=True)),
+    "quantize_ties_away": dict(quantize=_quantize_variant(ties_away=True)),
+    "quantize_limit_240": dict(quantize=_quantize_variant(limit=240.0)),
+    "rope_scaled": dict(fp8_decode=_decode_fp8_variant(rope_scaled=True)),
+    "scale_ignored": dict(fp8_decode=_decode_fp8_variant(scale_ignored=True)),
+}
+
+
+def test_unmutated_fp8_passes_its_pins():
+    assert _run_fp8_pins() == []
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_fp8_mutation_is_caught(name):
+    assert _run_fp8_pins(**FP8_MUTATIONS[name]), f"fp8 mutation {name} passed every pin"

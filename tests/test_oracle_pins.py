@@ -54,3 +54,15 @@ def test_absorb_end_to_end():
 
 def test_absorb_selection():
     P.pin_absorb_selection(oracle.absorb_q_ref, oracle.absorb_o_ref)
+
+
+def test_e4m3_table():
+    P.pin_e4m3_table(oracle.e4m3_decode)
+
+
+def test_e4m3_quantizer():
+    P.pin_e4m3_quantizer(oracle.quantize_e4m3_rows, oracle.e4m3_decode)
+
+
+def test_fp8_decode_matches_bf16():
+    P.pin_fp8_decode_matches_bf16(oracle.mla_decode_fp8_ref, oracle.mla_decode_ref)
