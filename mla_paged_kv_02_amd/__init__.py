@@ -26,8 +26,9 @@ from ._lib import MlaError, check, lib  # noqa: F401
 HEAD_DIM = 576
 HEAD_DIM_V = 512
 PAGE_SIZE = 64
+FP8_PAGE_BYTES = 41216   # 64 x 512 E4M3 latent + 64 x 64 BF16 rotary + 64 FP32 scales
 
-__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "kv_append", "absorb_q", "absorb_o", "split_metadata_host",
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "decode_fwd_fp8", "kv_append", "absorb_q", "absorb_o", "split_metadata_host",
            "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
 
 
@@ -117,12 +118,7 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
     lse [B, s_q, h_q] float32. Without ``meta`` the call builds the plan
     itself inside its workspace.
     """
-    dev = q.device
-    _require(q, "q", torch.bfloat16, ndim=4)
-    bsz, s_q, h_q, d = q.shape
-    if d != HEAD_DIM:
-        raise ValueError(f"q head dim must be {HEAD_DIM}, got {d}")
-    _require(kv_cache, "kv_cache", torch.bfloat16, device=dev)
+    _require(kv_cache, "kv_cache", torch.bfloat16, device=q.device)
     if kv_cache.dim() == 4:
         if tuple(kv_cache.shape[1:]) != (PAGE_SIZE, 1, HEAD_DIM):
             raise ValueError(f"kv_cache must be [num_pages, 64, 1, 576], got {tuple(kv_cache.shape)}")
@@ -131,6 +127,34 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
             raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
     else:
         raise ValueError("kv_cache must have 3 or 4 dims")
+    return _decode(lib().mla_decode_fwd, "mla_decode_fwd", q, kv_cache, block_table, seqlens, softmax_scale,
+                   causal, meta, out, lse, workspace, num_partitions)
+
+
+def decode_fwd_fp8(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
+                   seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                   meta: Optional[SplitMeta] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   num_partitions: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """decode_fwd over an FP8 latent cache (mla_decode_fwd_fp8): kv_pages is
+    uint8 [num_pages, 41216] in the page layout of include/mla_decode_fp8.h
+    (E4M3 latent rows, BF16 rotary rows, FP32 per-token scales). Query
+    blocks of h_q * s_q <= 64 rows."""
+    _require(kv_pages, "kv_pages", torch.uint8, device=q.device, ndim=2)
+    if kv_pages.shape[1] != FP8_PAGE_BYTES:
+        raise ValueError(f"kv_pages must be [num_pages, {FP8_PAGE_BYTES}], got {tuple(kv_pages.shape)}")
+    return _decode(lib().mla_decode_fwd_fp8, "mla_decode_fwd_fp8", q, kv_pages, block_table, seqlens,
+                   softmax_scale, causal, meta, out, lse, workspace, num_partitions)
+
+
+def _decode(fn, name, q, kv_cache, block_table, seqlens, softmax_scale, causal, meta, out, lse, workspace,
+            num_partitions):
+    dev = q.device
+    _require(q, "q", torch.bfloat16, ndim=4)
+    bsz, s_q, h_q, d = q.shape
+    if d != HEAD_DIM:
+        raise ValueError(f"q head dim must be {HEAD_DIM}, got {d}")
     _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
     _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
     if block_table.shape[0] != bsz or seqlens.shape[0] != bsz:
@@ -158,13 +182,13 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < need or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous buffer of >= {need} bytes")
-    status = lib().mla_decode_fwd(
+    status = fn(
         q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(), block_table.shape[1],
         seqlens.data_ptr(), bsz, s_q, h_q, kv_cache.shape[0], ctypes.c_float(softmax_scale),
         int(bool(causal)), meta.metadata.data_ptr() if meta is not None else None,
         num_partitions, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
-    check(status, "mla_decode_fwd")
+    check(status, name)
     return out, lse
 
 

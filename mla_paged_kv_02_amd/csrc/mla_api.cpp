@@ -4,6 +4,7 @@
 // per decode step, then run the attention call once per layer; the bridge
 // checks its inputs and orchestrates the kernels.
 #include "../../include/mla_decode.h"
+#include "../../include/mla_decode_fp8.h"
 
 #include <hip/hip_runtime.h>
 
@@ -240,11 +241,16 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
     return MLA_OK;
 }
 
-mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
-                          int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
-                          int h_q, int num_pages, float softmax_scale, int causal,
-                          int32_t* metadata, int num_partitions, void* workspace,
-                          size_t workspace_bytes_, void* out, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both decode entry points: the BF16 cache, or FP8 pages (16-row kernel only).
+mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* block_table,
+                           int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
+                           int h_q, int num_pages, float softmax_scale, int causal,
+                           int32_t* metadata, int num_partitions, void* workspace,
+                           size_t workspace_bytes_, void* out, float* lse, void* stream, bool fp8) {
     if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch < 1 || s_q < 1 || h_q < 1 || max_blocks_per_seq < 1 || num_pages < 1)
@@ -264,6 +270,10 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     if (!make_plan(batch, h_q, s_q, num_partitions,
                    num_partitions > 0 ? 0 : current_cu_count(), &pl))
         return MLA_ERR_UNSUPPORTED;
+    if (fp8) {
+        if (pl.kernel != DecodeKernel::Rows16) return MLA_ERR_UNSUPPORTED;
+        pl.kernel = DecodeKernel::Rows16Fp8;
+    }
     const WorkspaceLayout wl = workspace_layout(pl, metadata == nullptr);
     if (workspace_bytes_ < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
@@ -305,6 +315,30 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     if (!pl.fused_combine && launch_combine(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
     if (te && hipEventRecord(te->ev[2], st) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* block_table,
+                          int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
+                          int h_q, int num_pages, float softmax_scale, int causal,
+                          int32_t* metadata, int num_partitions, void* workspace,
+                          size_t workspace_bytes_, void* out, float* lse, void* stream) {
+    return decode_fwd_impl(q, kv_cache, block_table, max_blocks_per_seq, seqlens, batch, s_q, h_q, num_pages,
+                           softmax_scale, causal, metadata, num_partitions, workspace, workspace_bytes_, out,
+                           lse, stream, false);
+}
+
+mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t* block_table,
+                              int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q, int h_q,
+                              int num_pages, float softmax_scale, int causal, int32_t* metadata,
+                              int num_partitions, void* workspace, size_t workspace_bytes_, void* out,
+                              float* lse, void* stream) {
+    return decode_fwd_impl(q, kv_cache, block_table, max_blocks_per_seq, seqlens, batch, s_q, h_q, num_pages,
+                           softmax_scale, causal, metadata, num_partitions, workspace, workspace_bytes_, out,
+                           lse, stream, true);
 }
 
 mla_status mla_timing_enable(int enable) {

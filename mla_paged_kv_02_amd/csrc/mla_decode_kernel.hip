@@ -7,6 +7,7 @@ hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t s
     switch (plan.kernel) {
         case DecodeKernel::Rows16: return launch_decode_rows16(plan, args, stream);
         case DecodeKernel::WaveSplit: return launch_decode_ws(plan, args, stream);
+        case DecodeKernel::Rows16Fp8: return launch_decode_rows16_fp8(plan, args, stream);
     }
     return hipErrorInvalidValue;
 }

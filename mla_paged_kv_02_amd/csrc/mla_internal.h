@@ -11,8 +11,9 @@ namespace mla {
 // the M = h_q*s_q rows of a sequence, P partitions cut the page list, and
 // the grid is P*R workgroups.
 //   Rows16:    tm = 16, four waves each owning a key stripe of every page;
-//   WaveSplit: tm = 64, four score waves and four value waves.
-enum class DecodeKernel { Rows16, WaveSplit };
+//   WaveSplit: tm = 64, four score waves and four value waves;
+//   Rows16Fp8: the Rows16 organisation over the FP8 page format.
+enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8 };
 
 struct Plan {
     int batch, h_q, s_q, M;
@@ -63,6 +64,7 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_rows16_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 
 // Host build of the same plan (tests and host callers).

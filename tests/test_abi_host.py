@@ -169,3 +169,24 @@ def test_absorb_q_argument_checks(kw, status):
 ])
 def test_absorb_o_argument_checks(kw, status):
     assert _absorb_o(**kw) == status
+
+
+def _decode_fp8(**kw):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, maxb=4, seqlens=FAKE, batch=2, s_q=1, h_q=16,
+                pages=8, scale=1 / 24, causal=0, meta=FAKE, nparts=64, ws=FAKE,
+                ws_bytes=1 << 30, out=FAKE, lse=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_decode_fwd_fp8(
+        args["q"], args["kv"], args["bt"], args["maxb"], args["seqlens"], args["batch"],
+        args["s_q"], args["h_q"], args["pages"], ctypes.c_float(args["scale"]), args["causal"],
+        args["meta"], args["nparts"], args["ws"], args["ws_bytes"], args["out"], args["lse"],
+        args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv=None), INVALID), (dict(q=None), INVALID), (dict(batch=0), INVALID), (dict(causal=3), INVALID),
+    (dict(h_q=128), UNSUPPORTED), (dict(h_q=16, s_q=8), UNSUPPORTED),
+    (dict(kv=FAKE + 4), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED), (dict(ws_bytes=1024), TOO_SMALL),
+])
+def test_decode_fp8_argument_checks(kw, status):
+    assert _decode_fp8(**kw) == status

@@ -29,6 +29,9 @@ from .gen import (  # noqa: F401
     AbsorbInputs,
     make_absorb_inputs,
     make_absorb_workload,
+    FP8_PAGE_BYTES,
+    make_fp8_cache,
+    pack_fp8_pages,
 )
 from .roofline import (  # noqa: F401
     algorithmic_bytes,

@@ -295,3 +295,49 @@ def make_absorb_inputs(tokens: int, heads: int, d_nope: int, d_v: int, seed: int
 def make_absorb_workload(name: str) -> AbsorbInputs:
     w = ABSORB_WORKLOADS[name]
     return make_absorb_inputs(w["tokens"], w["heads"], w["d_nope"], w["d_v"], w["seed"])
+
+
+# FP8 latent caches (E4M3 latent bytes, BF16 rotary part, FP32 per-token
+# scales; page layout of include/mla_decode_fp8.h).
+FP8_PAGE_BYTES = 41216
+
+
+def _e4m3_grid():
+    """Finite non-negative E4M3 values and their codes, from the bit layout
+    (bias 7, 3 mantissa bits; exponent field 0 subnormal). Input drawing only."""
+    codes = np.arange(0x7F, dtype=np.int64)          # 0x00 .. 0x7E (0x7F is NaN)
+    exp, man = codes >> 3, codes & 7
+    vals = np.where(exp == 0, man / 8.0 * 2.0 ** -6, (1 + man / 8.0) * 2.0 ** (exp - 7))
+    return vals, codes.astype(np.uint8)
+
+
+def make_fp8_cache(inp: MlaInputs, seed: int):
+    """An FP8 cache for the pages of `inp`: latent bytes whose values are
+    about N(0,1) * 112 on the E4M3 grid (nearest grid point, drawn from
+    ``default_rng(seed)``), scales U[0.8, 1.2] * 4/448 so the latent values
+    are about N(0,1) like the BF16 workloads', each token at its own scale,
+    and the rotary part taken from inp's BF16 rows.
+    Returns (codes uint8 [P, 64, 512], rope uint16 [P, 64, 64],
+    scales float32 [P, 64])."""
+    rng = np.random.default_rng(seed)
+    pages = inp.kv_bits.shape[0]
+    y = rng.standard_normal((pages, PAGE_SIZE, 512), dtype=np.float32) * np.float32(112.0)
+    vals, codes = _e4m3_grid()
+    mag = np.minimum(np.abs(y), 448.0)
+    idx = np.clip(np.searchsorted(vals, mag), 1, vals.size - 1)
+    near = np.where(mag - vals[idx - 1] <= vals[idx] - mag, idx - 1, idx)
+    lat = codes[near] | np.where(y < 0, 0x80, 0).astype(np.uint8)
+    scales = (rng.uniform(0.8, 1.2, size=(pages, PAGE_SIZE)) * (4.0 / 448.0)).astype(np.float32)
+    rope = np.ascontiguousarray(inp.kv_bits[:, :, 0, HEAD_DIM_V:])
+    return lat.astype(np.uint8), rope, scales
+
+
+def pack_fp8_pages(codes: np.ndarray, rope: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """(codes [P,64,512] u8, rope [P,64,64] u16, scales [P,64] f32) -> the
+    device page layout, uint8 [P, 41216]."""
+    pages = codes.shape[0]
+    out = np.empty((pages, FP8_PAGE_BYTES), dtype=np.uint8)
+    out[:, :32768] = codes.reshape(pages, -1)
+    out[:, 32768:40960] = np.ascontiguousarray(rope, dtype=np.uint16).view(np.uint8).reshape(pages, -1)
+    out[:, 40960:] = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint8).reshape(pages, -1)
+    return out
