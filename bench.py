@@ -27,8 +27,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from workloads import (ABSORB_WORKLOADS, APPEND_WORKLOADS, MI355X_BF16_TFLOPS, MI355X_HBM_GBPS,  # noqa: E402
-                       WORKLOADS, algorithmic_bytes, algorithmic_flops, make_absorb_workload,
-                       make_append_workload, make_workload_inputs)
+                       WORKLOADS, algorithmic_bytes, algorithmic_bytes_fp8, algorithmic_flops,
+                       make_absorb_workload, make_append_workload, make_fp8_cache, make_workload_inputs,
+                       pack_fp8_pages)
 
 METRIC = "MLA paged decode: achieved HBM GB/s and TFLOP/s (% of MI355X peak)"
 DEFAULT_WORKLOAD = "memory_bound"
@@ -157,7 +158,9 @@ def cpu_baseline(workload: str, inp, budget_s: float):
 
 
 def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_bytes: int,
-                 num_partitions: int = 0):
+                 num_partitions: int = 0, fp8: bool = False):
+    """`fp8`: the same workload over an FP8 latent cache (mla_decode_fwd_fp8),
+    its latent values drawn at the same scale as the BF16 rows."""
     import torch
     import mla_paged_kv_02_amd as mla
 
@@ -165,10 +168,15 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     inp = make_workload_inputs(name)
     dev = torch.device("cuda:0")
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    kv0 = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    if fp8:
+        kv0 = torch.from_numpy(pack_fp8_pages(*make_fp8_cache(inp, seed=w.seed + 100))).to(dev)
+        decode = mla.decode_fwd_fp8
+    else:
+        kv0 = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        decode = mla.decode_fwd
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seqlens).to(dev)
-    kv_bytes = kv0.numel() * 2
+    kv_bytes = kv0.numel() * kv0.element_size()
     copies = max(1, min(16, math.ceil(rotate_bytes / max(kv_bytes, 1))))
     kvs = [kv0] + [kv0.clone() for _ in range(copies - 1)]
     out = torch.empty((inp.batch, w.s_q, w.h_q, 512), dtype=torch.bfloat16, device=dev)
@@ -183,8 +191,8 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions)
         if ev is not None:
             ev[0].record(stream)
-        mla.decode_fwd(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out,
-                       lse=lse, workspace=ws)
+        decode(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out,
+               lse=lse, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
 
@@ -218,7 +226,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     dec_ms = dec_ms_sum / steps
     comb_ms = comb_ms_sum / steps
 
-    nbytes = algorithmic_bytes(inp.seqlens, w.s_q, w.h_q)
+    nbytes = (algorithmic_bytes_fp8 if fp8 else algorithmic_bytes)(inp.seqlens, w.s_q, w.h_q)
     flops = algorithmic_flops(inp.seqlens, w.s_q, w.h_q, w.causal)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -227,7 +235,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     dec_gbps = nbytes / (dec_ms * 1e-3) / 1e9
     dec_tflops = flops / (dec_ms * 1e-3) / 1e12
     hbm_bound = nbytes * 1.0 / (MI355X_HBM_GBPS * 1e9) >= flops * 1.0 / (MI355X_BF16_TFLOPS * 1e12)
-    cnt = counter_entry(name)
+    cnt = counter_entry(name + "_fp8" if fp8 else name)
     traffic = cnt.get("bytes_per_call") if cnt else None
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": MI355X_HBM_GBPS,
@@ -238,7 +246,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
                 "unit": "TFLOP/s", "frac": round(dec_tflops / MI355X_BF16_TFLOPS, 4),
                 "traffic": traffic}
     line = {
-        "metric": METRIC,
+        "metric": METRIC if not fp8 else "MLA paged decode over an FP8 latent cache: achieved HBM GB/s",
         "value": round(gbps, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -248,10 +256,12 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded; BF16 N(0,1) query and cache, shuffled block table)",
-        "config": {"workload": f"{name}: {w.description}, d=576, dv=512, page 64, "
-                               f"{'causal' if w.causal else 'non-causal'}",
+        "dtype": "bf16" if not fp8 else "fp8-e4m3 cache, bf16 arithmetic",
+        "data": ("synthetic (seeded; BF16 N(0,1) query and cache, shuffled block table)" if not fp8 else
+                 "synthetic (seeded; BF16 N(0,1) query; E4M3 latent values ~N(0,1) at per-token scales, "
+                 "BF16 rotary part; shuffled block table)"),
+        "config": {"workload": f"{name}{'_fp8' if fp8 else ''}: {w.description}, d=576, dv=512, page 64, "
+                               f"{'fp8 latent cache, ' if fp8 else ''}{'causal' if w.causal else 'non-causal'}",
                    "batch": inp.batch, "s_q": w.s_q, "h_q": w.h_q,
                    "total_tokens": int(inp.seqlens.sum()), "seed": w.seed},
         "tflops": round(tflops, 2),
@@ -632,9 +642,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="one of %s, or 'all'; with --op kv_append one of %s or 'all'"
                          % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
-    ap.add_argument("--op", default="decode", choices=("decode", "kv_append", "absorb"),
-                    help="decode (the hot path; default), the paged cache append, or the absorption "
-                         "products")
+    ap.add_argument("--op", default="decode", choices=("decode", "decode_fp8", "kv_append", "absorb"),
+                    help="decode (the hot path; default), decode over an FP8 latent cache (workloads "
+                         "with h_q * s_q <= 64), the paged cache append, or the absorption products")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
@@ -688,12 +698,16 @@ def main():
         for name in names:
             print(json.dumps(run_append(name, args.steps, args.warmup)), flush=True)
         return
+    fp8 = args.op == "decode_fp8"
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
+    if fp8:
+        names = [n for n in names if WORKLOADS[n].h_q * WORKLOADS[n].s_q <= 64]
     ctx = None if args.no_stream_context else streaming_context()
     for name in names:
         line = run_workload(name, args.steps, args.warmup,
-                            args.cpu_budget if name == DEFAULT_WORKLOAD or args.workload != "all" else 0,
-                            int(args.rotate_gib * (1 << 30)), args.num_partitions)
+                            args.cpu_budget if (name == DEFAULT_WORKLOAD or args.workload != "all") and not fp8
+                            else 0,
+                            int(args.rotate_gib * (1 << 30)), args.num_partitions, fp8=fp8)
         if ctx:
             line["achievable_context"] = ctx
         print(json.dumps(line), flush=True)

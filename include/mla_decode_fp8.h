@@ -13,10 +13,14 @@
  * token t is e4m3(byte[t][d]) * scale[t]. The 64 rotary values stay BF16.
  *
  * Page layout (64 tokens, MLA_FP8_PAGE_BYTES = 41,216 bytes, contiguous):
+ * four groups of 16 tokens, group k (tokens 16k .. 16k+15) at 10,304 k,
+ * each holding, for its tokens r = 0..15,
  *
- *   bytes [0, 32768)        latent: token r's 512 E4M3 bytes at 512 r
- *   bytes [32768, 40960)    rotary: token r's 64 BF16 values at 32768 + 128 r
- *   bytes [40960, 41216)    scales: token r's FP32 scale at 40960 + 4 r
+ *   bytes [0, 8192)         latent: token r's 512 E4M3 bytes at 512 r
+ *   bytes [8192, 10240)     rotary: token r's 64 BF16 values at 8192 + 128 r
+ *   bytes [10240, 10304)    scales: token r's FP32 scale at 10240 + 4 r
+ *
+ * (a group is what one wave of the kernel streams, scales included)
  *
  * Everything else (metadata, query, output, lse, workspace, split plan,
  * calling pattern, masking, empty rows, errors) is exactly as for

@@ -4,16 +4,18 @@
 // The cache keeps only the latent row (page "MLA 和 MHA 的 Kernel 区别",
 // section "内存布局和 KV Cache 大小"), so storing it in 8 bits cuts the
 // bytes decode must stream, which is what bounds it. Page layout (64 tokens,
-// 41,216 bytes): the 64 latent rows as OCP E4M3 bytes (512 each), then the
-// 64 rotary parts in BF16 (128 bytes each), then 64 FP32 per-token scales.
-// The value of latent coordinate d of token t is e4m3(byte) * scale[t].
+// 41,216 bytes): four groups of 16 tokens, 10,304 bytes each, holding the 16
+// latent rows as OCP E4M3 bytes (512 each), then their rotary parts in BF16
+// (128 bytes each), then their 16 FP32 scales. The value of latent
+// coordinate d of token t is e4m3(byte) * scale[t]. A group is exactly one
+// wave's stripe, so its scales arrive with its rows.
 //
 // Same organisation as the BF16 16-row kernel (four waves, each streaming
 // its own 16-key stripe of every page through a private double buffer, no
 // barrier in the page loop), with three changes:
 //
-//  * a stripe is 10 KB: 8 KB of E4M3 latent rows and 2 KB of rotary rows;
-//    the 16 scales come through the scalar cache;
+//  * a stripe is one group: 8 KB of E4M3 latent rows, 2 KB of rotary rows
+//    and the 64-byte scale block (a four-lane load);
 //  * after its stripe lands, a wave converts the latent bytes to BF16 into a
 //    private 16 KB buffer (row stride 1 KB, chunk c of row r at c ^ (r & 7))
 //    with the hardware's packed FP8->BF16 conversion; E4M3 values are exact
@@ -38,7 +40,6 @@ __device__ __forceinline__ int ld_const_i(const int32_t* p, size_t i) {
         reinterpret_cast<uintptr_t>(p))[i];
 }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -46,18 +47,18 @@ constexpr int kWaves = 4;
 constexpr int kSRows = 16;                          // keys per stripe
 constexpr int kLatBytes = 512;                      // E4M3 latent row
 constexpr int kRopeBytes = 128;                     // BF16 rotary row
-constexpr int kRopeOff = kPageRows * kLatBytes;     // 32768
-constexpr int kScaleOff = kRopeOff + kPageRows * kRopeBytes;   // 40960
-constexpr int kF8PageBytes = kScaleOff + kPageRows * 4;        // 41216
-constexpr int kStripeLat = kSRows * kLatBytes;      // 8192
-constexpr int kStripeRope = kSRows * kRopeBytes;    // 2048
-constexpr int kStripeBytes = kStripeLat + kStripeRope;         // 10240
-constexpr int kSLoads = kStripeBytes / 1024;        // 10 wave loads per stripe
+constexpr int kStripeLat = kSRows * kLatBytes;      // 8192: latent rows of a group
+constexpr int kStripeRope = kSRows * kRopeBytes;    // 2048: rotary rows
+constexpr int kScaleOffG = kStripeLat + kStripeRope;           // 10240: scales
+constexpr int kStripeBytes = kScaleOffG + kSRows * 4;          // 10304 per group / LDS slot
+constexpr int kF8PageBytes = 4 * kStripeBytes;      // 41216
+constexpr int kSLoads = 11;                         // 10 wave loads of 1 KB + the scale block
 constexpr int kCvtRow = 1024;                       // BF16 latent row in LDS
 constexpr int kCvtBytes = kSRows * kCvtRow;         // 16384
-constexpr int kWaveLds = 2 * kStripeBytes + kCvtBytes;         // 36864
+constexpr int kWaveLds = 2 * kStripeBytes + kCvtBytes;         // 36992
 constexpr int kNDT = kHeadDimV / 16;                // 32 output tiles of 16 columns
 constexpr int kQLatSteps = kHeadDimV / 32;          // 16
+constexpr int kQLdsSteps = kQLatSteps - 1;          // 15 latent k-steps in LDS, the last in VGPRs
 constexpr int kQRopeSteps = 2;
 constexpr float kRefMargin = 32.f;
 constexpr float kHeadroom = 64.f;
@@ -65,6 +66,7 @@ constexpr float kHeadroom = 64.f;
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 constexpr int kWaitStripe = wait_vm_lgkm0(kSLoads);
 constexpr int kWaitAll = wait_vm_lgkm0(0);
+constexpr int kWaitLgkm = wait_vm_lgkm0(63);                   // lgkmcnt(0) only
 
 template <int kImm>
 __device__ __forceinline__ void wait_then_fence() {
@@ -92,9 +94,11 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const uint32_t (&w)[4], bf16x8& 
 }  // namespace
 
 __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a) {
-    // per wave: two 10 KB stripe buffers, then the 16 KB BF16 latent buffer
-    __shared__ __attribute__((aligned(1024))) uint8_t wlds[kWaves][kWaveLds];
-    __shared__ __attribute__((aligned(16))) uint8_t qlds[kQLatSteps * 1024];
+    // per wave: two stripe buffers, then the 16 KB BF16 latent buffer; the
+    // query's latent k-steps 0..14 (its last latent k-step and its rotary
+    // part are held in registers), which makes room for the scale blocks
+    __shared__ __attribute__((aligned(16))) uint8_t wlds[kWaves][kWaveLds];
+    __shared__ __attribute__((aligned(16))) uint8_t qlds[kQLdsSteps * 1024];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -125,44 +129,48 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a
     const uint32_t mine1_lds = lds_addr_of(mine1);
     const uint32_t qlds_lds = lds_addr_of(qlds);
 
-    // Stripe gather: wave load j < 8 brings latent bytes 1024 j .. of the
-    // stripe (rows 2j, 2j+1), loads 8 and 9 the rotary rows 8(j-8) .. +7.
-    // Rows at or past the sequence end read row 0 of the page (always
-    // valid): finite data whose softmax weight is zero.
+    // Stripe gather (the wave's group, a copy of its layout): wave load
+    // j < 8 brings latent bytes 1024 j .. (rows 2j, 2j+1), loads 8 and 9 the
+    // rotary rows 8(j-8) .. +7, and lanes 0..3 bring the 64-byte scale block.
+    // Rows at or past the sequence end read token 0 of the page (always
+    // valid): finite data whose softmax weight is zero. Their scales are
+    // read as stored and never used.
     auto issue_stripe = [&](const uint8_t* page, int valid, uint32_t dst) {
-        const uint32_t lat0 = (uint32_t)(wave * kStripeLat);
-        const uint32_t rope0 = (uint32_t)(kRopeOff + wave * kStripeRope);
+        const uint32_t g0 = (uint32_t)(wave * kStripeBytes);
         if (valid >= kSRows) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) load_lds16_untracked(page, lat0 + j * 1024 + lane * 16, dst + j * 1024);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                load_lds16_untracked(page, rope0 + j * 1024 + lane * 16, dst + kStripeLat + j * 1024);
+            for (int j = 0; j < 10; ++j) load_lds16_untracked(page, g0 + j * 1024 + lane * 16, dst + j * 1024);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int r = 2 * j + (lane >> 5);
-                const uint32_t off = r < valid ? lat0 + j * 1024 + lane * 16 : (uint32_t)((lane & 31) * 16);
+                const uint32_t off = r < valid ? g0 + j * 1024 + lane * 16 : (uint32_t)((lane & 31) * 16);
                 load_lds16_untracked(page, off, dst + j * 1024);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int r = 8 * j + (lane >> 3);
-                const uint32_t off = r < valid ? rope0 + j * 1024 + lane * 16 : (uint32_t)(kRopeOff + (lane & 7) * 16);
+                const uint32_t off = r < valid ? g0 + kStripeLat + j * 1024 + lane * 16
+                                               : (uint32_t)(kStripeLat + (lane & 7) * 16);
                 load_lds16_untracked(page, off, dst + kStripeLat + j * 1024);
             }
         }
+        if (lane < 4) load_lds16_untracked(page, g0 + kScaleOffG + lane * 16, dst + kScaleOffG);
     };
 
     // Conversion of the stripe's latent bytes: pass it (0..7) takes row
     // 2 it + lane/32, E4M3 chunk lane%32 (16 values), and writes BF16 chunks
     // 2c, 2c+1 of that row, each at its swizzled slot.
     auto convert_stripe = [&](const uint8_t* src) {
+        // all eight reads first, so their latencies overlap
+        u32x4 raw[8];
+#pragma unroll
+        for (int it = 0; it < 8; ++it) raw[it] = *(const MLA_AS3 u32x4*)(src + it * 1024 + lane * 16);
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int r = 2 * it + (lane >> 5);
             const int c = lane & 31;
-            const u32x4 v = *(const MLA_AS3 u32x4*)(src + it * 1024 + lane * 16);
+            const u32x4 v = raw[it];
             const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
             bf16x8 lo, hi;
             e4m3x16_to_bf16(w, lo, hi);
@@ -202,51 +210,59 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a
             return reinterpret_cast<const uint8_t*>(a.kv) + (size_t)phys * kF8PageBytes;
         };
         auto stripe_valid = [&](int pn) { return nseq - pn * kPageRows - wave * kSRows; };
-        // the 16 scales of this wave's stripe of a page, through the scalar cache
-        auto load_scales = [&](int phys) {
-            return *reinterpret_cast<const __attribute__((address_space(4))) f32x16*>(
-                reinterpret_cast<uintptr_t>(page_ptr(phys) + kScaleOff + wave * kSRows * 4));
-        };
 
         {
             const uint16_t* q_blk = a.q + ((size_t)b * a.M + rb * 16) * kHeadDim;
             const uint32_t q_off = (uint32_t)(((row_ok ? i16 : 0) * kHeadDim + g * 8) * 2);
+            // latent k-steps 4w .. 4w+3 below 15 into the shared buffer; the
+            // last latent k-step and the two rotary ones into this wave's
+            // second stripe buffer, to be read into registers
 #pragma unroll
             for (int i = 0; i < kQLatSteps / kWaves; ++i) {
                 const int ks = wave * (kQLatSteps / kWaves) + i;
-                load_lds16_untracked(q_blk, q_off + ks * 64, qlds_lds + ks * 1024);
+                if (ks < kQLdsSteps) load_lds16_untracked(q_blk, q_off + ks * 64, qlds_lds + ks * 1024);
             }
 #pragma unroll
-            for (int i = 0; i < kQRopeSteps; ++i)
-                load_lds16_untracked(q_blk, q_off + (kQLatSteps + i) * 64, mine1_lds + i * 1024);
+            for (int i = 0; i < 1 + kQRopeSteps; ++i)
+                load_lds16_untracked(q_blk, q_off + (kQLdsSteps + i) * 64, mine1_lds + i * 1024);
         }
-        int phys0 = ld_const_i(bt_row, lo);
-        issue_stripe(page_ptr(phys0), stripe_valid(lo), mine0_lds);
-        int phys1 = ld_const_i(bt_row, lo + 1 < hi ? lo + 1 : lo);
+        // Two stripes are in flight while a page is computed: a page's stripe
+        // buffer is free once its latent bytes are converted and its rotary
+        // rows and scales are in registers, so the stripe two pages ahead
+        // goes into it then. The second buffer holds the query's last latent
+        // and rotary k-steps until they are in registers.
+        issue_stripe(page_ptr(ld_const_i(bt_row, lo)), stripe_valid(lo), mine0_lds);
+        int phys2 = ld_const_i(bt_row, lo + 1 < hi ? lo + 1 : lo);
         wait_then_fence<kWaitStripe>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        const bf16x8 qlast = lds_read16(mine1 + lane * 16);
         bf16x8 qr[kQRopeSteps];
 #pragma unroll
-        for (int i = 0; i < kQRopeSteps; ++i) qr[i] = lds_read16(mine1 + i * 1024 + lane * 16);
-        wait_then_fence<kWaitStripe>();
+        for (int i = 0; i < kQRopeSteps; ++i) qr[i] = lds_read16(mine1 + (1 + i) * 1024 + lane * 16);
+        wait_then_fence<kWaitLgkm>();
+        if (lo + 1 < hi) issue_stripe(page_ptr(phys2), stripe_valid(lo + 1), mine1_lds);
+        phys2 = ld_const_i(bt_row, lo + 2 < hi ? lo + 2 : hi - 1);
 
         const int L = a.causal ? min(max(nseq - a.s_q + tok + 1, 0), nseq) : nseq;
         float m_ref = -INFINITY, l_run = 0.f;
         const bool full = (lo == 0) && (hi == npages);
         const int slotno = full ? 0 : ld_const_i(seqinfo, 4 * b + 0) + (p - ld_const_i(seqinfo, 4 * b + 1));
 
-        // page pn (physical phys0) has its stripe in `cur`; the next page's
-        // (phys1) is issued into `nxt` first, and the entry after that read
-        auto page_step = [&](int pn, uint8_t* cur, uint32_t nxt_lds) -> int {
-            const bool more = pn + 1 < hi;
-            if (more) issue_stripe(page_ptr(phys1), stripe_valid(pn + 1), nxt_lds);
-            const f32x16 sc16 = load_scales(phys0);
-            phys0 = phys1;
-            phys1 = ld_const_i(bt_row, pn + 2 < hi ? pn + 2 : hi - 1);
-            if (more) wait_then_fence<kWaitStripe>();
+        // Page pn: its stripe is in `cur` (stripe pn+1, if any, behind it).
+        auto page_step = [&](int pn, uint8_t* cur, uint32_t cur_lds) -> int {
+            if (pn + 1 < hi) wait_then_fence<kWaitStripe>();
             else wait_then_fence<kWaitAll>();
+            // rotary K fragments and the lane's four key scales to registers,
+            // the latent bytes converted; then the buffer takes stripe pn+2
+            bf16x8 kr[kQRopeSteps];
+#pragma unroll
+            for (int i = 0; i < kQRopeSteps; ++i) kr[i] = lds_read16(cur + rofs + i * 64);
+            const f32x4 sc4 = *(const MLA_AS3 f32x4*)(cur + kScaleOffG + 16 * g);
             convert_stripe(cur);
+            wait_then_fence<kWaitLgkm>();
+            if (pn + 2 < hi) issue_stripe(page_ptr(phys2), stripe_valid(pn + 2), cur_lds);
+            phys2 = ld_const_i(bt_row, pn + 3 < hi ? pn + 3 : hi - 1);
 
             // ---- S^T = K Q^T: latent (scaled below) and rotary parts apart
             f32x4 s_lat = {0.f, 0.f, 0.f, 0.f}, s_rope = {0.f, 0.f, 0.f, 0.f};
@@ -261,27 +277,21 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a
                 }
 #pragma unroll
                 for (int ks = 0; ks < kQLatSteps; ++ks) {
-                    s_lat = mfma16(kf[ks % KD], qf[ks % KD], s_lat);
-                    if (ks + KD < kQLatSteps) {
-                        kf[ks % KD] = lds_read16(cvt + k_off(ks + KD));
-                        qf[ks % KD] = lds_read16(q_frag + (ks + KD) * 1024);
-                    }
+                    s_lat = mfma16(kf[ks % KD], ks < kQLdsSteps ? qf[ks % KD] : qlast, s_lat);
+                    if (ks + KD < kQLatSteps) kf[ks % KD] = lds_read16(cvt + k_off(ks + KD));
+                    if (ks + KD < kQLdsSteps) qf[ks % KD] = lds_read16(q_frag + (ks + KD) * 1024);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int i = 0; i < kQRopeSteps; ++i)
-                    s_rope = mfma16(lds_read16(cur + rofs + i * 64), qr[i], s_rope);
+                for (int i = 0; i < kQRopeSteps; ++i) s_rope = mfma16(kr[i], qr[i], s_rope);
             }
 
             // ---- mask, per-token scale, reference check (log2 domain)
             const int key0 = pn * kPageRows + wave * kSRows + 4 * g;
+            // lane group g holds keys 4g..4g+3 of the stripe
             float sck[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // lane group g holds keys 4g..4g+3 of the stripe
-                const float v = g == 0 ? sc16[j] : g == 1 ? sc16[4 + j] : g == 2 ? sc16[8 + j] : sc16[12 + j];
-                sck[j] = (key0 + j < L) ? v : 0.f;
-            }
+            for (int j = 0; j < 4; ++j) sck[j] = (key0 + j < L) ? sc4[j] : 0.f;
             f32x4 s;
             float mx = -INFINITY;
 #pragma unroll
@@ -331,17 +341,19 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a
             l_run = 0.f;
             int pn = lo;
             while (true) {
-                pn = page_step(pn, mine0, mine1_lds);
+                pn = page_step(pn, mine0, mine0_lds);
                 if (pn < 0 || pn >= hi) break;
-                pn = page_step(pn, mine1, mine0_lds);
+                pn = page_step(pn, mine1, mine1_lds);
                 if (pn < 0 || pn >= hi) break;
             }
             restart = pn < 0;
+            // after a restart the stripes in flight must land before the
+            // buffers are reused
             wait_then_fence<kWaitAll>();
             if (restart) {
-                phys0 = ld_const_i(bt_row, lo);
-                issue_stripe(page_ptr(phys0), stripe_valid(lo), mine0_lds);
-                phys1 = ld_const_i(bt_row, lo + 1 < hi ? lo + 1 : lo);
+                issue_stripe(page_ptr(ld_const_i(bt_row, lo)), stripe_valid(lo), mine0_lds);
+                if (lo + 1 < hi) issue_stripe(page_ptr(ld_const_i(bt_row, lo + 1)), stripe_valid(lo + 1), mine1_lds);
+                phys2 = ld_const_i(bt_row, lo + 2 < hi ? lo + 2 : hi - 1);
             }
         } while (restart);
 

@@ -35,6 +35,7 @@ from .gen import (  # noqa: F401
 )
 from .roofline import (  # noqa: F401
     algorithmic_bytes,
+    algorithmic_bytes_fp8,
     algorithmic_flops,
     visible_lengths,
     MI355X_HBM_GBPS,

@@ -334,10 +334,11 @@ def make_fp8_cache(inp: MlaInputs, seed: int):
 
 def pack_fp8_pages(codes: np.ndarray, rope: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """(codes [P,64,512] u8, rope [P,64,64] u16, scales [P,64] f32) -> the
-    device page layout, uint8 [P, 41216]."""
+    device page layout, uint8 [P, 41216]: four groups of 16 tokens, 10,304
+    bytes each, holding the group's latent rows, rotary rows, scales."""
     pages = codes.shape[0]
-    out = np.empty((pages, FP8_PAGE_BYTES), dtype=np.uint8)
-    out[:, :32768] = codes.reshape(pages, -1)
-    out[:, 32768:40960] = np.ascontiguousarray(rope, dtype=np.uint16).view(np.uint8).reshape(pages, -1)
-    out[:, 40960:] = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint8).reshape(pages, -1)
-    return out
+    g = np.empty((pages, 4, 10304), dtype=np.uint8)
+    g[:, :, :8192] = codes.reshape(pages, 4, 8192)
+    g[:, :, 8192:10240] = np.ascontiguousarray(rope, dtype=np.uint16).view(np.uint8).reshape(pages, 4, 2048)
+    g[:, :, 10240:] = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint8).reshape(pages, 4, 64)
+    return g.reshape(pages, FP8_PAGE_BYTES)

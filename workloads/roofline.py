@@ -41,13 +41,23 @@ def visible_lengths(seqlens, s_q: int, causal: bool) -> np.ndarray:
     return np.broadcast_to(n, (n.shape[0], s_q)).copy()
 
 
-def algorithmic_bytes(seqlens, s_q: int, h_q: int) -> int:
+# FP8 cache row: 512 E4M3 latent bytes, 64 BF16 rotary values, one FP32 scale
+_FP8_ROW_BYTES = 512 + 64 * 2 + 4
+
+
+def algorithmic_bytes(seqlens, s_q: int, h_q: int, row_bytes: int = _ROW_BYTES) -> int:
+    """`row_bytes` is what one cached token costs: 1152 for the BF16 cache,
+    644 for the FP8 cache (``algorithmic_bytes_fp8``)."""
     seqlens = np.asarray(seqlens, dtype=np.int64)
     b = seqlens.size
     rows = b * s_q * h_q
     pages = int(((seqlens + 63) // 64).sum())
-    return int(_ROW_BYTES * int(seqlens.sum()) + _ROW_BYTES * rows + _OUT_BYTES * rows
+    return int(row_bytes * int(seqlens.sum()) + _ROW_BYTES * rows + _OUT_BYTES * rows
                + 4 * rows + 4 * pages + 4 * b)
+
+
+def algorithmic_bytes_fp8(seqlens, s_q: int, h_q: int) -> int:
+    return algorithmic_bytes(seqlens, s_q, h_q, _FP8_ROW_BYTES)
 
 
 def algorithmic_flops(seqlens, s_q: int, h_q: int, causal: bool) -> int:
