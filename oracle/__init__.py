@@ -30,4 +30,5 @@ from .fp8_ref import (  # noqa: F401
     quantize_e4m3_rows,
     dequantize_fp8_cache,
     mla_decode_fp8_ref,
+    kv_append_fp8_ref,
 )

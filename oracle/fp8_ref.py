@@ -20,10 +20,11 @@ Readings where the pages leave it open:
 * Decode over this cache is decode over the dequantised rows: every formula
   of the BF16 reference applies unchanged to the rows
   [decode(bytes) * scale ; rope].
-* The quantiser (used to make test caches from real-valued rows) takes
-  scale = amax / 448 over the token's 512 values (zero rows get scale 1)
-  and rounds x / scale to the nearest E4M3 value, ties to the even
-  mantissa, never overflowing past 448.
+* The quantiser (the cache writer's rule) takes scale = amax / 448 over the
+  token's 512 values (zero rows get scale 1) and rounds x / scale to the
+  nearest E4M3 value, ties to the even mantissa, saturating at 448; the
+  scale and the quotient are FP32 operations, as in the kernel that writes
+  the cache.
 """
 
 from __future__ import annotations
@@ -58,33 +59,32 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 
 def quantize_e4m3_rows(rows: np.ndarray):
-    """rows [N, 512] real -> (codes uint8 [N, 512], scale float32 [N]).
+    """rows [N, 512] (values exact in float32, e.g. BF16 inputs) ->
+    (codes uint8 [N, 512], scale float32 [N]).
 
-    scale = amax / 448 per row (1 for an all-zero row), then x / scale is
-    rounded to the nearest finite E4M3 value, ties to even mantissa."""
-    rows = np.asarray(rows, dtype=np.float64)
-    amax = np.abs(rows).max(axis=1)
-    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
-    # the stored scale is FP32; quantise against exactly that value
-    y = rows / scale.astype(np.float64)[:, None]
-    finite = np.array([b for b in range(256) if not math.isnan(_E4M3_TABLE[b])])
-    vals = _E4M3_TABLE[finite]
-    order = np.argsort(vals, kind="stable")
-    vals, codes_sorted = vals[order], finite[order]
-    # drop the duplicate zero (0x80, -0) so every value appears once
-    keep = np.ones(vals.size, dtype=bool)
-    keep[(vals == 0.0) & (codes_sorted == 0x80)] = False
-    vals, codes_sorted = vals[keep], codes_sorted[keep]
-    idx = np.clip(np.searchsorted(vals, y), 1, vals.size - 1)
-    lo, hi = vals[idx - 1], vals[idx]
-    pick_hi = (hi - y) < (y - lo)
-    tie = (hi - y) == (y - lo)
-    even_hi = (codes_sorted[idx] & 1) == 0
-    pick_hi = pick_hi | (tie & even_hi)
-    out_idx = np.where(pick_hi, idx, idx - 1)
-    out_idx = np.where(y >= vals[-1], vals.size - 1, out_idx)
-    out_idx = np.where(y <= vals[0], 0, out_idx)
-    return codes_sorted[out_idx].astype(np.uint8).reshape(rows.shape), scale
+    Every step is taken in FP32, as a kernel writing the cache would take it
+    (a quantised code is an integer decided by floating point, so both sides
+    decide it in the same precision): scale = fl32(amax / 448) per row (1 for
+    an all-zero row), y = fl32(x / scale), then y is rounded to the nearest
+    E4M3 value, ties to the even mantissa, magnitudes above 448 saturating
+    to 448. The sign bit is y's (so a negative value that rounds to zero is
+    0x80, negative zero)."""
+    x = np.asarray(rows, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[:, None]).astype(np.float32)
+    mag = np.abs(y).astype(np.float64)
+    grid = _E4M3_TABLE[:0x7F]                      # codes 0x00..0x7E, increasing
+    idx = np.clip(np.searchsorted(grid, mag), 1, grid.size - 1)
+    lo, hi = grid[idx - 1], grid[idx]
+    pick_hi = (hi - mag) < (mag - lo)
+    tie = (hi - mag) == (mag - lo)
+    pick_hi = pick_hi | (tie & (idx % 2 == 0))     # code idx is even
+    code = np.where(pick_hi, idx, idx - 1)
+    code = np.where(mag >= grid[-1], 0x7E, code)
+    code = np.where(mag <= 0.0, 0, code)
+    neg = np.signbit(y)
+    return (code | np.where(neg, 0x80, 0)).astype(np.uint8), scale
 
 
 def dequantize_fp8_cache(latent_codes: np.ndarray, rope_bits: np.ndarray, scales: np.ndarray) -> np.ndarray:
@@ -116,3 +116,34 @@ def mla_decode_fp8_ref(q_bits, latent_codes, rope_bits, scales, block_table, seq
     kv = dequantize_fp8_cache(latent_codes, rope_bits, scales)
     return mla_decode_ref_f64(q.astype(np.float64), kv, table, seqlens,
                               float(np.float32(scale)), causal, seqs)
+
+
+def kv_append_fp8_ref(latent_codes, rope_bits, scales, new_bits, block_table, seqlens):
+    """Append into an FP8 cache: the placement of ``kv_append_ref`` (token i
+    of a sequence holding N tokens after the append goes to position
+    N - s_new + i; negative positions dropped, missing pages counted), each
+    placed token's latent part quantised by ``quantize_e4m3_rows`` and its
+    rotary part copied. Returns (codes, rope, scales, skipped), new arrays."""
+    codes = np.array(latent_codes, copy=True)
+    rope = np.array(rope_bits, copy=True)
+    sc = np.array(scales, copy=True)
+    bsz, s_new, _ = new_bits.shape
+    width = block_table.shape[1]
+    x = (np.asarray(new_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    skipped = 0
+    for b in range(bsz):
+        n = int(seqlens[b])
+        for i in range(s_new):
+            pos = n - s_new + i
+            if pos < 0:
+                continue
+            logical = pos // 64
+            page = int(block_table[b, logical]) if logical < width else -1
+            if page < 0 or page >= codes.shape[0]:
+                skipped += 1
+                continue
+            q, s1 = quantize_e4m3_rows(x[b, i:i + 1, :512])
+            codes[page, pos % 64] = q[0]
+            sc[page, pos % 64] = s1[0]
+            rope[page, pos % 64] = new_bits[b, i, 512:]
+    return codes, rope, sc, skipped

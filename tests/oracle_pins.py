@@ -390,3 +390,65 @@ def pin_fp8_decode_matches_bf16(decode_fp8, ref_bits, seed=35):
     o1, l1 = decode_fp8(inp.q_bits, codes, rope, scales, inp.block_table, inp.seqlens, inp.scale, True)
     o2, l2 = ref_bits(inp.q_bits, kv_bits, inp.block_table, inp.seqlens, inp.scale, True)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "FP8 decode differs from BF16 decode"
+
+
+# (r) Quantiser against brute force: for every value, the code whose E4M3
+# value is nearest to |y| = |fl32(x / fl32(amax / 448))| (all 127 magnitudes
+# tried in a plain loop; ties to the even code; above 448 saturating to
+# 0x7E), with y's sign bit. Rows mix tiny values (subnormal codes, negative
+# values that round to zero), exact midpoints and the row maximum.
+def pin_e4m3_quantizer_bruteforce(quantize, decode, seed=36):
+    rng = np.random.default_rng(seed)
+    rows = (rng.standard_normal((3, 512)) * np.array([1.0, 1e-3, 50.0])[:, None]).astype(np.float32)
+    rows[0, :8] = [448.0, -1e-9, 1e-9, 2.0 ** -10, -(2.0 ** -10), 7.5 * 2 ** -9, 0.0, -0.0]
+    codes, scale = quantize(rows)
+    mags = [float(decode(np.array([c], dtype=np.uint8))[0]) for c in range(0x7F)]
+    for r in range(rows.shape[0]):
+        s32 = np.float32(np.abs(rows[r]).max()) / np.float32(448.0)
+        assert scale[r] == s32, "scale must be fl32(amax / 448)"
+        for d in range(0, 512, 7):
+            y = float(np.float32(rows[r, d]) / s32)
+            a = abs(y)
+            best = 0x7E if a >= 448.0 else None
+            if best is None:
+                dist = [abs(m - a) for m in mags]
+                dmin = min(dist)
+                cands = [c for c in range(0x7F) if dist[c] == dmin]
+                best = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+            want = best | (0x80 if math.copysign(1.0, y) < 0 else 0)
+            assert codes[r, d] == want, f"row {r} col {d}: y={y!r} code 0x{codes[r, d]:02x} want 0x{want:02x}"
+
+
+# (s) FP8 append from the physical side, as (k): every page row the placement
+# rule sends a token to holds that token's quantised latent bytes, its scale
+# and its rotary bits; every other row is unchanged; tokens without a page
+# are counted.
+def pin_append_fp8_physical_view(append_fp8, quantize, seed=37):
+    for inp in _append_cases(seed):
+        pages = inp.kv_bits.shape[0]
+        rng = np.random.default_rng(seed)
+        codes0 = rng.integers(0, 256, size=(pages, PAGE, 512)).astype(np.uint8)
+        rope0 = inp.kv_bits[:, :, 0, 512:].copy()
+        sc0 = rng.random((pages, PAGE)).astype(np.float32)
+        c1, r1, s1, skipped = append_fp8(codes0, rope0, sc0, inp.new_bits, inp.block_table, inp.seqlens)
+        ec, er, es = codes0.copy(), rope0.copy(), sc0.copy()
+        s_new = inp.new_bits.shape[1]
+        written = 0
+        for b in range(inp.block_table.shape[0]):
+            first_new = int(inp.seqlens[b]) - s_new
+            for logical in range(inp.block_table.shape[1]):
+                page = int(inp.block_table[b, logical])
+                if not 0 <= page < pages:
+                    continue
+                for slot in range(PAGE):
+                    i = logical * PAGE + slot - first_new
+                    if 0 <= i < s_new:
+                        x = bf16_bits_to_f32(inp.new_bits[b, i, :512])[None]
+                        q, sq = quantize(x)
+                        ec[page, slot], es[page, slot] = q[0], sq[0]
+                        er[page, slot] = inp.new_bits[b, i, 512:]
+                        written += 1
+        placed = sum(min(int(n), s_new) for n in inp.seqlens)
+        assert np.array_equal(c1, ec) and np.array_equal(r1, er), "latent or rotary rows wrong"
+        assert np.array_equal(s1.view(np.uint32), es.view(np.uint32)), "scales wrong"
+        assert skipped == placed - written

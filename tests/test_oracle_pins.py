@@ -66,3 +66,11 @@ def test_e4m3_quantizer():
 
 def test_fp8_decode_matches_bf16():
     P.pin_fp8_decode_matches_bf16(oracle.mla_decode_fp8_ref, oracle.mla_decode_ref)
+
+
+def test_e4m3_quantizer_bruteforce():
+    P.pin_e4m3_quantizer_bruteforce(oracle.quantize_e4m3_rows, oracle.e4m3_decode)
+
+
+def test_append_fp8_physical_view():
+    P.pin_append_fp8_physical_view(oracle.kv_append_fp8_ref, oracle.quantize_e4m3_rows)
