@@ -62,6 +62,25 @@ mla_status mla_kv_append(const void* new_rows, int batch, int s_new, const int32
                          const int32_t* block_table, int max_blocks_per_seq, void* kv_cache,
                          int num_pages, int32_t* skipped_rows, void* stream);
 
+/*
+ * mla_kv_append_fp8 - the same append into an FP8 cache (page layout of
+ * mla_decode_fp8.h): each placed token's 512 latent values are quantised
+ * with one FP32 scale, its 64 rotary values copied as BF16, and the scale
+ * stored in its group. Quantisation of a row x (BF16 values, exact in FP32):
+ *
+ *   scale = fl32(amax / 448) (amax = max |x_d|; 1 for an all-zero row)
+ *   y_d   = fl32(x_d / scale)
+ *   byte  = the E4M3 value nearest |y_d|, ties to the even mantissa,
+ *           magnitudes past 448 saturating to 448; sign bit of y_d
+ *
+ * Arguments as for mla_kv_append, with kv_pages device bytes
+ * [num_pages][MLA_FP8_PAGE_BYTES], 16-byte aligned, in place of kv_cache.
+ * Limits: batch * s_new * 72 < 2^31.
+ */
+mla_status mla_kv_append_fp8(const void* new_rows, int batch, int s_new, const int32_t* seqlens,
+                             const int32_t* block_table, int max_blocks_per_seq, void* kv_pages,
+                             int num_pages, int32_t* skipped_rows, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ HEAD_DIM_V = 512
 PAGE_SIZE = 64
 FP8_PAGE_BYTES = 41216   # 64 x 512 E4M3 latent + 64 x 64 BF16 rotary + 64 FP32 scales
 
-__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "decode_fwd_fp8", "kv_append", "absorb_q", "absorb_o", "split_metadata_host",
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "decode_fwd_fp8", "kv_append", "kv_append_fp8", "absorb_q", "absorb_o", "split_metadata_host",
            "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
 
 
@@ -224,6 +224,35 @@ def kv_append(new_rows: torch.Tensor, seqlens: torch.Tensor, block_table: torch.
                               skipped.data_ptr() if skipped is not None else None, _stream_ptr(dev)),
           "mla_kv_append")
     return kv_cache
+
+
+def kv_append_fp8(new_rows: torch.Tensor, seqlens: torch.Tensor, block_table: torch.Tensor,
+                  kv_pages: torch.Tensor, skipped: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kv_append into an FP8 cache (mla_kv_append_fp8): each placed token's
+    latent part is quantised to E4M3 with one FP32 scale, its rotary part
+    copied. kv_pages uint8 [num_pages, 41216], updated in place. Returns
+    kv_pages."""
+    dev = new_rows.device
+    _require(new_rows, "new_rows", torch.bfloat16, ndim=3)
+    bsz, s_new, d = new_rows.shape
+    if d != HEAD_DIM:
+        raise ValueError(f"new_rows head dim must be {HEAD_DIM}, got {d}")
+    _require(kv_pages, "kv_pages", torch.uint8, device=dev, ndim=2)
+    if kv_pages.shape[1] != FP8_PAGE_BYTES:
+        raise ValueError(f"kv_pages must be [num_pages, {FP8_PAGE_BYTES}], got {tuple(kv_pages.shape)}")
+    _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
+    _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != bsz or seqlens.shape[0] != bsz:
+        raise ValueError("block_table and seqlens must have one row per sequence")
+    if skipped is not None:
+        _require(skipped, "skipped", torch.int32, device=dev)
+        if skipped.numel() != 1:
+            raise ValueError("skipped must hold one int32")
+    check(lib().mla_kv_append_fp8(new_rows.data_ptr(), bsz, s_new, seqlens.data_ptr(), block_table.data_ptr(),
+                                  block_table.shape[1], kv_pages.data_ptr(), kv_pages.shape[0],
+                                  skipped.data_ptr() if skipped is not None else None, _stream_ptr(dev)),
+          "mla_kv_append_fp8")
+    return kv_pages
 
 
 def absorb_q(q_nope: torch.Tensor, q_rope: torch.Tensor, w_uk: torch.Tensor,

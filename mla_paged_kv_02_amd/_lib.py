@@ -32,6 +32,8 @@ SIGNATURES = {
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_kv_append": (_c_int, [_c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr]),
+    "mla_kv_append_fp8": (_c_int, [_c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_ptr,
+                                   _c_ptr]),
     "mla_absorb_q": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_ptr]),
     "mla_absorb_o": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_ptr]),
     "mla_decode_fwd_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,

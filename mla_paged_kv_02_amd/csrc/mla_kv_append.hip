@@ -10,6 +10,7 @@
 // kernel is bound by HBM and, for one decode step's few rows, by launch
 // latency.
 #include "../../include/mla_kv_append.h"
+#include "../../include/mla_decode_fp8.h"
 
 #include <hip/hip_runtime.h>
 
@@ -79,6 +80,88 @@ __global__ __launch_bounds__(kAppendThreads) void mla_kv_append_kernel(AppendArg
     if (missing && a.skipped) atomicAdd(a.skipped, missing);
 }
 
+// ---- appending into the FP8 page layout --------------------------------------
+//
+// One wave per new token: lane l holds latent values 8l..8l+7 (16 bytes of
+// the BF16 row), lanes 0..7 also its rotary chunk l. The row's largest
+// magnitude comes from a wave reduction; scale = amax / 448 and
+// y = x / scale are FP32 divisions (correctly rounded), and y is rounded to
+// E4M3 in integer arithmetic: magnitudes at or past 448 saturate to 448;
+// below 2^-6 the code is rint(|y| * 2^9) (subnormal steps of 2^-9); above,
+// |y| * 2^(3 - e) lies in [8, 16) for e = floor(log2 |y|) and rint of it
+// gives the mantissa (a carry to 16 moves to the next binade by itself:
+// code = 8 (e + 7) + r - 8). rint rounds half to even; the sign bit is y's.
+constexpr int kAppendF8Threads = 256;   // four tokens per workgroup
+
+struct AppendF8Args {
+    const uint16_t* src;     // [batch][s_new][576] BF16
+    uint8_t* pages;          // [num_pages][MLA_FP8_PAGE_BYTES]
+    const int32_t* seqlens;
+    const int32_t* block_table;
+    int32_t* skipped;
+    int batch, s_new, max_blocks, num_pages, tokens;
+};
+
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    uint32_t mag;
+    if (!(a < 448.f)) {
+        mag = 0x7Eu;
+    } else if (a < 0x1p-6f) {
+        mag = (uint32_t)rintf(a * 0x1p9f);
+    } else {
+        const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;    // -6 .. 8
+        const float r = rintf(ldexpf(a, 3 - e));                          // 8 .. 16
+        mag = (uint32_t)(8 * (e + 7) + (int)r - 8);
+        mag = mag > 0x7Eu ? 0x7Eu : mag;
+    }
+    return sign | mag;
+}
+
+__global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(AppendF8Args a) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * (kAppendF8Threads / 64) + (threadIdx.x >> 6);   // token of this wave
+    if (t >= a.tokens) return;
+    const int b = t / a.s_new;
+    const int i = t - b * a.s_new;
+    const int p = a.seqlens[b] - a.s_new + i;
+    if (p < 0) return;
+    const int blk = p >> 6;
+    const int page = blk < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + blk] : -1;
+    if (page < 0 || page >= a.num_pages) {
+        if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);
+        return;
+    }
+    const uint16_t* row = a.src + (size_t)t * kHeadDim;
+    const u32x4 lat = *reinterpret_cast<const u32x4*>(row + 8 * lane);
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(lat[k] << 16);
+        x[2 * k + 1] = __uint_as_float(lat[k] & 0xFFFF0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k] / scale) << (8 * k);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k] / scale) << (8 * k);
+    const int slot = p & (kPageRows - 1);
+    uint8_t* grp = a.pages + (size_t)page * MLA_FP8_PAGE_BYTES + (slot >> 4) * (MLA_FP8_PAGE_BYTES / 4);
+    const int r = slot & 15;
+    *reinterpret_cast<uint2*>(grp + r * 512 + 8 * lane) = uint2{lo, hi};
+    if (lane < 8)
+        *reinterpret_cast<u32x4*>(grp + 8192 + r * 128 + 16 * lane) =
+            *reinterpret_cast<const u32x4*>(row + 512 + 8 * lane);
+    if (lane == 0) *reinterpret_cast<float*>(grp + 10240 + 4 * r) = scale;
+}
+
 bool aligned_to(const void* p, size_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; }
 
 }  // namespace
@@ -109,6 +192,36 @@ extern "C" mla_status mla_kv_append(const void* new_rows, int batch, int s_new, 
     a.total_chunks = (int)chunks;
     const unsigned grid = (unsigned)((chunks + kAppendChunksPerBlock - 1) / kAppendChunksPerBlock);
     hipLaunchKernelGGL(mla_kv_append_kernel, dim3(grid), dim3(kAppendThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream), a);
+    return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+extern "C" mla_status mla_kv_append_fp8(const void* new_rows, int batch, int s_new, const int32_t* seqlens,
+                                        const int32_t* block_table, int max_blocks_per_seq, void* kv_pages,
+                                        int num_pages, int32_t* skipped_rows, void* stream) {
+    using namespace mla;
+    if (!new_rows || !seqlens || !block_table || !kv_pages) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || s_new < 1 || max_blocks_per_seq < 1 || num_pages < 1) return MLA_ERR_INVALID_ARG;
+    const long long tokens = (long long)batch * s_new;
+    if (tokens * kRowChunks >= (1LL << 31)) return MLA_ERR_UNSUPPORTED;
+    if ((long long)max_blocks_per_seq * batch > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+    if (!aligned_to(new_rows, 16) || !aligned_to(kv_pages, 16)) return MLA_ERR_MISALIGNED;
+    if (!aligned_to(seqlens, 4) || !aligned_to(block_table, 4) || (skipped_rows && !aligned_to(skipped_rows, 4)))
+        return MLA_ERR_MISALIGNED;
+    AppendF8Args a{};
+    a.src = static_cast<const uint16_t*>(new_rows);
+    a.pages = static_cast<uint8_t*>(kv_pages);
+    a.seqlens = seqlens;
+    a.block_table = block_table;
+    a.skipped = skipped_rows;
+    a.batch = batch;
+    a.s_new = s_new;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_pages = num_pages;
+    a.tokens = (int)tokens;
+    const int per_block = kAppendF8Threads / 64;
+    const unsigned grid = (unsigned)((tokens + per_block - 1) / per_block);
+    hipLaunchKernelGGL(mla_kv_append_fp8_kernel, dim3(grid), dim3(kAppendF8Threads), 0,
                        reinterpret_cast<hipStream_t>(stream), a);
     return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }

@@ -136,3 +136,68 @@ def test_fp8_rejects_large_query_blocks():
     sl = torch.from_numpy(inp.seqlens).cuda()
     with pytest.raises(mla.MlaError, match="UNSUPPORTED"):
         mla.decode_fwd_fp8(q, pages, bt, sl, inp.scale, False)
+
+
+def _append_fp8_case(inp, tag, count=True):
+    """Append into an FP8 cache on the GPU; the whole page buffer must equal
+    the oracle's pages bit for bit, and the skipped count must match."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    log(f"[case] fp8 append {tag} B={inp.batch} s_new={inp.s_new} pages={inp.kv_bits.shape[0]}")
+    codes, rope, scales = make_fp8_cache(inp, seed=460)
+    pages = torch.from_numpy(pack_fp8_pages(codes, rope, scales)).cuda()
+    new = torch.from_numpy(np.ascontiguousarray(inp.new_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    bt = torch.from_numpy(np.ascontiguousarray(inp.block_table)).cuda()
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    skipped = torch.zeros((), dtype=torch.int32, device="cuda") if count else None
+    mla.kv_append_fp8(new, sl, bt, pages, skipped)
+    torch.cuda.synchronize()
+    rc, rr, rs, rskip = oracle.kv_append_fp8_ref(codes, rope, scales, inp.new_bits, inp.block_table, inp.seqlens)
+    got = pages.cpu().numpy()
+    want = pack_fp8_pages(rc, rr, rs)
+    bad = np.argwhere(np.any(got != want, axis=1))
+    assert bad.size == 0, f"{len(bad)} pages differ, first {bad[:4].ravel().tolist()}"
+    if count:
+        assert int(skipped.item()) == rskip
+    return rc, rr, rs
+
+
+@pytest.mark.parametrize("s_new", [1, 3, 70])
+def test_fp8_append_ragged(s_new):
+    from workloads import make_append_inputs
+    inp = make_append_inputs([0, 1, 5, 63, 64, 65, 130, 333], s_new, seed=470 + s_new, extra_blocks=1)
+    _append_fp8_case(inp, f"ragged s_new={s_new}")
+
+
+def test_fp8_append_holes_and_extremes():
+    import oracle_pins as P
+    for k, inp in enumerate(P._append_cases(seed=480)):
+        nb = inp.new_bits.copy()
+        # zero rows, a row with one huge value, tiny and negative-zero values
+        nb[0, 0, :512] = 0
+        nb[0, 1, :512] = 0x0001
+        nb[0, 1, 7] = 0x7F00
+        nb[0, 2, :512] = 0x8000
+        _append_fp8_case(type(inp)(inp.seqlens, inp.block_table, inp.kv_bits, nb), f"holes[{k}]")
+
+
+def test_fp8_append_workload_and_decode():
+    """The chunked-prefill append into an FP8 cache, then decode of the last
+    tokens over it, against the oracle's cache and decode."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from workloads import make_append_inputs
+    from workloads import AppendInputs
+    seqlens = [300, 64, 2, 129, 1000]
+    s_q = 4
+    dec = make_inputs(seqlens, s_q, 16, seed=491, causal=True)
+    new_bits = make_append_inputs(seqlens, s_q, seed=490).new_bits
+    inp = AppendInputs(dec.seqlens, dec.block_table, dec.kv_bits, new_bits)
+    rc, rr, rs = _append_fp8_case(inp, "then decode")
+    _check(dec, rc, rr, rs, "decode after fp8 append")
+
+
+def test_fp8_append_full_size():
+    from workloads import make_append_workload
+    inp = make_append_workload("append_prefill_chunk")
+    _append_fp8_case(inp, "append_prefill_chunk")
