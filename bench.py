@@ -77,7 +77,7 @@ def counter_entry(workload: str):
 
 
 def _op_of(workload: str) -> str:
-    if workload in APPEND_WORKLOADS:
+    if workload in APPEND_WORKLOADS or workload.replace("_fp8", "") in APPEND_WORKLOADS:
         return "kv_append"
     if workload in ABSORB_WORKLOADS:
         return "absorb"
@@ -312,10 +312,10 @@ def hold_queue(ms: float):
     torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
 
 
-def append_bytes(inp) -> int:
+def append_bytes(inp, fp8: bool = False) -> int:
     """Algorithmic bytes of one cache append: each placed token's row read once
-    and written once (2 x 1152 B), one block-table entry per (sequence, page)
-    touched, and the lengths."""
+    (1152 B) and written once (1152 B, or 644 B into an FP8 cache), one
+    block-table entry per (sequence, page) touched, and the lengths."""
     s_new = inp.s_new
     rows, pages = 0, 0
     for n in inp.seqlens:
@@ -324,10 +324,10 @@ def append_bytes(inp) -> int:
         if hi > lo:
             rows += hi - lo
             pages += (hi - 1) // 64 - lo // 64 + 1
-    return 2 * 1152 * rows + 4 * pages + 4 * inp.batch
+    return (1152 + (644 if fp8 else 1152)) * rows + 4 * pages + 4 * inp.batch
 
 
-def run_append(name: str, steps: int, warmup: int):
+def run_append(name: str, steps: int, warmup: int, fp8: bool = False):
     """One step = one mla_kv_append call on the workload's new rows. Each call
     writes the same rows (idempotent), timed call by call with HIP events on
     the launch stream, behind a device-side spin that keeps the host's launch
@@ -341,20 +341,25 @@ def run_append(name: str, steps: int, warmup: int):
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    kv = to_dev(inp.kv_bits)
+    if fp8:
+        kv = torch.from_numpy(pack_fp8_pages(*make_fp8_cache(inp, seed=APPEND_WORKLOADS[name]["seed"] + 100))).to(dev)
+        append = mla.kv_append_fp8
+    else:
+        kv = to_dev(inp.kv_bits)
+        append = mla.kv_append
     new = to_dev(inp.new_bits)
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seqlens).to(dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
-        mla.kv_append(new, sl, bt, kv)
+        append(new, sl, bt, kv)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     hold_queue(0.1 * steps)
     t0.record(stream)
     for _ in range(steps):
-        mla.kv_append(new, sl, bt, kv)
+        append(new, sl, bt, kv)
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
@@ -362,26 +367,27 @@ def run_append(name: str, steps: int, warmup: int):
     hold_queue(0.1 * steps)
     for a, b in evs:
         a.record(stream)
-        mla.kv_append(new, sl, bt, kv)
+        append(new, sl, bt, kv)
         b.record(stream)
     torch.cuda.synchronize()
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    nbytes = append_bytes(inp)
+    nbytes = append_bytes(inp, fp8)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
     # the kernel's duration for the roofline: the back-to-back average (an
     # event pair around every call adds a few microseconds of its own, which
     # is most of a one-decode-step append)
     kern_gbps = gbps
-    cnt = counter_entry(name)
+    cnt = counter_entry(name + "_fp8" if fp8 else name)
     traffic = cnt.get("bytes_per_call") if cnt else None
     w = APPEND_WORKLOADS[name]
     return {
-        "metric": "paged latent-cache append: achieved HBM GB/s",
+        "metric": "paged latent-cache append" + (" into an FP8 cache (quantising)" if fp8 else "")
+                  + ": achieved HBM GB/s",
         "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; BF16 N(0,1) new rows, shuffled block table)",
-        "config": {"workload": f"{name}: batch {inp.batch}, {w['s_new']} new tokens per sequence, "
+        "config": {"workload": f"{name}{'_fp8' if fp8 else ''}: batch {inp.batch}, {w['s_new']} new tokens per sequence, "
                                f"final lengths U[{w['lengths'][2]},{w['lengths'][3]}], rows of 576 bf16, page 64",
                    "batch": inp.batch, "s_new": inp.s_new, "seed": w["seed"]},
         "append_kernel_us_avg": round(ms_step * 1e3, 2),
@@ -642,7 +648,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="one of %s, or 'all'; with --op kv_append one of %s or 'all'"
                          % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
-    ap.add_argument("--op", default="decode", choices=("decode", "decode_fp8", "kv_append", "absorb"),
+    ap.add_argument("--op", default="decode",
+                    choices=("decode", "decode_fp8", "kv_append", "kv_append_fp8", "absorb"),
                     help="decode (the hot path; default), decode over an FP8 latent cache (workloads "
                          "with h_q * s_q <= 64), the paged cache append, or the absorption products")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -693,10 +700,11 @@ def main():
             print(json.dumps(run_absorb(name, args.steps, args.warmup, int(args.rotate_gib * (1 << 30)))),
                   flush=True)
         return
-    if args.op == "kv_append":
+    if args.op in ("kv_append", "kv_append_fp8"):
         names = list(APPEND_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]
         for name in names:
-            print(json.dumps(run_append(name, args.steps, args.warmup)), flush=True)
+            print(json.dumps(run_append(name, args.steps, args.warmup, fp8=args.op == "kv_append_fp8")),
+                  flush=True)
         return
     fp8 = args.op == "decode_fp8"
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]

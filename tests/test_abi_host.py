@@ -190,3 +190,17 @@ def _decode_fp8(**kw):
 ])
 def test_decode_fp8_argument_checks(kw, status):
     assert _decode_fp8(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(new=None), INVALID), (dict(kv=None), INVALID), (dict(s_new=0), INVALID), (dict(pages=0), INVALID),
+    (dict(batch=1 << 16, s_new=1 << 15), UNSUPPORTED), (dict(kv=FAKE + 8), MISALIGNED),
+    (dict(skipped=FAKE + 1), MISALIGNED),
+])
+def test_append_fp8_argument_checks(kw, status):
+    args = dict(new=FAKE, batch=2, s_new=3, seqlens=FAKE, bt=FAKE, maxb=4, kv=FAKE, pages=8,
+                skipped=None, stream=None)
+    args.update(kw)
+    assert _lib.lib().mla_kv_append_fp8(args["new"], args["batch"], args["s_new"], args["seqlens"], args["bt"],
+                                        args["maxb"], args["kv"], args["pages"], args["skipped"],
+                                        args["stream"]) == status
