@@ -32,3 +32,4 @@ from .fp8_ref import (  # noqa: F401
     mla_decode_fp8_ref,
     kv_append_fp8_ref,
 )
+from .mha_ref import mha_decode_ref, mha_decode_bruteforce  # noqa: F401

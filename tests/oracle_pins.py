@@ -452,3 +452,47 @@ def pin_append_fp8_physical_view(append_fp8, quantize, seed=37):
         assert np.array_equal(c1, ec) and np.array_equal(r1, er), "latent or rotary rows wrong"
         assert np.array_equal(s1.view(np.uint32), es.view(np.uint32)), "scales wrong"
         assert skipped == placed - written
+
+
+# (t) MHA decode against brute force: pure-Python fsum loops on tiny shapes,
+# grouped heads, causal and not, a sequence shorter than s_q.
+def pin_mha_bruteforce(mha, seed=38):
+    from workloads import make_mha_inputs
+    for causal in (False, True):
+        inp = make_mha_inputs([3, 70, 1], 2, 4, 2, 16, seed + causal, causal=causal)
+        o, l = mha(inp.q_bits, inp.k_bits, inp.v_bits, inp.block_table, inp.seqlens, inp.scale, causal)
+        f = lambda bits: bf16_bits_to_f32(bits).astype(np.float64)
+        ob, lb = oracle.mha_decode_bruteforce(f(inp.q_bits), f(inp.k_bits), f(inp.v_bits), inp.block_table,
+                                              inp.seqlens, float(np.float32(inp.scale)), causal)
+        assert np.abs(o - ob).max() < 1e-12, "MHA output vs brute force"
+        fin = np.isfinite(lb)
+        assert np.array_equal(fin, np.isfinite(l)) and np.abs(l[fin] - lb[fin]).max() < 1e-12
+
+
+# (u) Grouping: giving every query head its own copy of its group's KV head
+# (H_kv = H_q) leaves every output unchanged; a single cached token returns
+# its value vector; relabelling physical pages changes nothing.
+def pin_mha_grouping_and_invariants(mha, seed=39):
+    import dataclasses
+    from workloads import make_mha_inputs, permute_pages
+    inp = make_mha_inputs([37, 100, 64, 129], 1, 8, 2, 32, seed)
+    o1, l1 = mha(inp.q_bits, inp.k_bits, inp.v_bits, inp.block_table, inp.seqlens, inp.scale, False)
+    k_full = np.repeat(inp.k_bits, 4, axis=2)
+    v_full = np.repeat(inp.v_bits, 4, axis=2)
+    o2, l2 = mha(inp.q_bits, k_full, v_full, inp.block_table, inp.seqlens, inp.scale, False)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "grouping"
+    one = make_mha_inputs([1, 1], 1, 4, 2, 32, seed + 1)
+    o3, _ = mha(one.q_bits, one.k_bits, one.v_bits, one.block_table, one.seqlens, one.scale, False)
+    for b in range(2):
+        page = one.block_table[b, 0]
+        for h in range(4):
+            assert np.array_equal(o3[b, 0, h], bf16_bits_to_f32(one.v_bits[page, 0, h // 2]).astype(np.float64))
+    # page relabelling: permute_pages moves MlaInputs' kv_bits; move K and V alike
+    rng = np.random.default_rng(seed + 2)
+    pi = rng.permutation(inp.k_bits.shape[0])
+    k_p = np.empty_like(inp.k_bits)
+    v_p = np.empty_like(inp.v_bits)
+    k_p[pi], v_p[pi] = inp.k_bits, inp.v_bits
+    table = np.where(inp.block_table >= 0, pi[np.maximum(inp.block_table, 0)], inp.block_table).astype(np.int32)
+    o4, l4 = mha(inp.q_bits, k_p, v_p, table, inp.seqlens, inp.scale, False)
+    assert np.array_equal(o1, o4) and np.array_equal(l1, l4), "page relabelling"

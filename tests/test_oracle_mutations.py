@@ -340,3 +340,64 @@ def test_unmutated_fp8_passes_its_pins():
 @pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
 def test_fp8_mutation_is_caught(name):
     assert _run_fp8_pins(**FP8_MUTATIONS[name]), f"fp8 mutation {name} passed every pin"
+
+
+# ---- MHA contrast ----------------------------------------------------------------
+
+def _mha_variant(group_fn=None, swap_kv=False, no_scale=False, causal_shift=0):
+    def mha(q_bits, k_bits, v_bits, table, seqlens, scale, causal):
+        f = lambda bits: (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(
+            np.float32).astype(np.float64)
+        q, k, v = f(q_bits), f(k_bits), f(v_bits)
+        if swap_kv:
+            k, v = v, k
+        bsz, s_q, h_q, d = q.shape
+        h_kv = k.shape[2]
+        group = h_q // h_kv
+        sc = 1.0 if no_scale else float(np.float32(scale))
+        out = np.zeros((bsz, s_q, h_q, d))
+        lse = np.full((bsz, s_q, h_q), -np.inf)
+        for b in range(bsz):
+            n = int(seqlens[b])
+            for i in range(s_q):
+                L = max(0, min(n, n - s_q + i + 1 + causal_shift)) if causal else n
+                for h in range(h_q):
+                    if L == 0:
+                        continue
+                    kv = group_fn(h, group, h_kv) if group_fn else h // group
+                    t = np.arange(L)
+                    pages = np.asarray(table[b])[t // 64]
+                    s = sc * (k[pages, t % 64, kv] @ q[b, i, h])
+                    m = s.max()
+                    e = np.exp(s - m)
+                    lse[b, i, h] = m + math.log(e.sum())
+                    out[b, i, h] = (e / e.sum()) @ v[pages, t % 64, kv]
+        return out, lse
+    return mha
+
+
+MHA_MUTATIONS = {
+    "interleaved_groups": _mha_variant(group_fn=lambda h, g, hkv: h % hkv),
+    "k_v_swapped": _mha_variant(swap_kv=True),
+    "scale_missing": _mha_variant(no_scale=True),
+    "causal_off_by_one": _mha_variant(causal_shift=-1),
+}
+
+
+def _run_mha_pins(fn):
+    failed = []
+    for name, pin in [("bruteforce", P.pin_mha_bruteforce), ("grouping", P.pin_mha_grouping_and_invariants)]:
+        try:
+            pin(fn)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            failed.append(name)
+    return failed
+
+
+def test_unmutated_mha_passes_its_pins():
+    assert _run_mha_pins(oracle.mha_decode_ref) == []
+
+
+@pytest.mark.parametrize("name", sorted(MHA_MUTATIONS))
+def test_mha_mutation_is_caught(name):
+    assert _run_mha_pins(MHA_MUTATIONS[name]), f"MHA mutation {name} passed every pin"

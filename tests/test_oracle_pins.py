@@ -74,3 +74,11 @@ def test_e4m3_quantizer_bruteforce():
 
 def test_append_fp8_physical_view():
     P.pin_append_fp8_physical_view(oracle.kv_append_fp8_ref, oracle.quantize_e4m3_rows)
+
+
+def test_mha_bruteforce():
+    P.pin_mha_bruteforce(oracle.mha_decode_ref)
+
+
+def test_mha_grouping_and_invariants():
+    P.pin_mha_grouping_and_invariants(oracle.mha_decode_ref)

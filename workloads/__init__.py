@@ -32,6 +32,10 @@ from .gen import (  # noqa: F401
     FP8_PAGE_BYTES,
     make_fp8_cache,
     pack_fp8_pages,
+    MhaInputs,
+    MHA_WORKLOADS,
+    make_mha_inputs,
+    make_mha_workload,
 )
 from .roofline import (  # noqa: F401
     algorithmic_bytes,

@@ -342,3 +342,50 @@ def pack_fp8_pages(codes: np.ndarray, rope: np.ndarray, scales: np.ndarray) -> n
     g[:, :, 8192:10240] = np.ascontiguousarray(rope, dtype=np.uint16).view(np.uint8).reshape(pages, 4, 2048)
     g[:, :, 10240:] = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint8).reshape(pages, 4, 64)
     return g.reshape(pages, FP8_PAGE_BYTES)
+
+
+# Paged multi-head (grouped-query) attention inputs, the contrast case:
+# keys and values [num_pages][64][H_kv][D] each, drawn like the MLA cache.
+@dataclasses.dataclass
+class MhaInputs:
+    seqlens: np.ndarray        # int32 [B]
+    block_table: np.ndarray    # int32 [B, max_blocks]
+    q_bits: np.ndarray         # uint16 [B, S_q, H_q, D]
+    k_bits: np.ndarray         # uint16 [NB, 64, H_kv, D]
+    v_bits: np.ndarray         # uint16 [NB, 64, H_kv, D]
+    scale: float
+    causal: bool
+
+    @property
+    def batch(self) -> int:
+        return int(self.seqlens.shape[0])
+
+
+def make_mha_inputs(seqlens: Sequence[int], s_q: int, h_q: int, h_kv: int, d: int, seed: int,
+                    causal: bool = False, rng: Optional[np.random.Generator] = None) -> MhaInputs:
+    """Steps 1-3 of the recipe for lengths, pages and table; then q, K and V
+    N(0,1) rounded to BF16 from the same stream; scale 1/sqrt(D)."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    base = make_inputs(seqlens, 1, 1, seed, rng=rng)
+    nb = base.kv_bits.shape[0]
+    q = _standard_normal_bf16(rng, (base.batch, s_q, h_q, d))
+    k = _standard_normal_bf16(rng, (nb, PAGE_SIZE, h_kv, d))
+    v = _standard_normal_bf16(rng, (nb, PAGE_SIZE, h_kv, d))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    return MhaInputs(base.seqlens, base.block_table, q, k, v, scale, bool(causal))
+
+
+# The contrast workload: the memory-bound decode step (64 sequences,
+# lengths U[3072, 5120], 16 query heads) under grouped-query MHA with 8 KV
+# heads of 128 values, the layout an MHA model of this size would cache.
+MHA_WORKLOADS = {
+    "mha_memory_bound": dict(seed=25, batch=64, lengths=(3072, 5120), s_q=1, h_q=16, h_kv=8, d=128),
+}
+
+
+def make_mha_workload(name: str) -> MhaInputs:
+    w = MHA_WORKLOADS[name]
+    rng = np.random.default_rng(w["seed"])
+    seqlens = rng.integers(w["lengths"][0], w["lengths"][1], size=w["batch"], endpoint=True).astype(np.int32)
+    return make_mha_inputs(seqlens, w["s_q"], w["h_q"], w["h_kv"], w["d"], w["seed"], rng=rng)
