@@ -26,7 +26,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from workloads import (ABSORB_WORKLOADS, APPEND_WORKLOADS, MI355X_BF16_TFLOPS, MI355X_HBM_GBPS,  # noqa: E402
+from workloads import (ABSORB_WORKLOADS, APPEND_WORKLOADS, MHA_WORKLOADS, MI355X_BF16_TFLOPS,  # noqa: E402
+                       MI355X_HBM_GBPS, make_mha_workload, visible_lengths,
                        WORKLOADS, algorithmic_bytes, algorithmic_bytes_fp8, algorithmic_flops,
                        make_absorb_workload, make_append_workload, make_fp8_cache, make_workload_inputs,
                        pack_fp8_pages)
@@ -40,7 +41,8 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # Sources of the ops beside decode; the decode path's digest leaves their
 # kernels out, so that changing one op does not void another's counter figures.
 OP_SOURCES = {"kv_append": ("mla_kv_append.hip", "mla_common.h"),
-              "absorb": ("mla_absorb.hip", "mla_common.h")}
+              "absorb": ("mla_absorb.hip", "mla_common.h"),
+              "mha": ("mla_mha_decode.hip", "mla_common.h")}
 
 
 def kernel_digest(op: str = "decode") -> str:
@@ -79,6 +81,8 @@ def counter_entry(workload: str):
 def _op_of(workload: str) -> str:
     if workload in APPEND_WORKLOADS or workload.replace("_fp8", "") in APPEND_WORKLOADS:
         return "kv_append"
+    if workload in MHA_WORKLOADS:
+        return "mha"
     if workload in ABSORB_WORKLOADS:
         return "absorb"
     return "decode"
@@ -516,6 +520,67 @@ def run_absorb(name: str, steps: int, warmup: int, rotate_bytes: int):
     }
 
 
+def run_mha(name: str, steps: int, warmup: int):
+    """One step = one paged grouped-query MHA decode call over the contrast
+    workload (the memory-bound sequences with 8 KV heads of 128 values:
+    a 1.09 GB K+V cache, so no step finds the previous one's data in the
+    MALL). Timed back to back between two events behind a device-side spin."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+
+    w = MHA_WORKLOADS[name]
+    inp = make_mha_workload(name)
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = to_dev(inp.q_bits), to_dev(inp.k_bits), to_dev(inp.v_bits)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seqlens).to(dev)
+    out = torch.empty((inp.batch, w["s_q"], w["h_q"], w["d"]), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.batch, w["s_q"], w["h_q"]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        mla.mha_decode_fwd(q, k, v, bt, sl, inp.scale, inp.causal, out=out, lse=lse)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(0.1 * steps)
+    t0.record(stream)
+    for _ in range(steps):
+        mla.mha_decode_fwd(q, k, v, bt, sl, inp.scale, inp.causal, out=out, lse=lse)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    n = inp.seqlens.astype(np.int64)
+    rows = inp.batch * w["s_q"] * w["h_q"]
+    kv_bytes = 2 * w["h_kv"] * w["d"] * 2 * int(n.sum())
+    nbytes = kv_bytes + 2 * 2 * rows * w["d"] + 4 * rows + 4 * int(((n + 63) // 64).sum()) + 4 * inp.batch
+    flops = 2 * 2 * w["d"] * w["h_q"] * int(visible_lengths(n, w["s_q"], False).sum())
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    mla_bytes = algorithmic_bytes(inp.seqlens, w["s_q"], w["h_q"])
+    cnt = counter_entry(name)
+    return {
+        "metric": "paged GQA MHA decode (contrast to MLA): achieved HBM GB/s",
+        "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded; BF16 N(0,1) query, keys and values, shuffled block table)",
+        "config": {"workload": f"{name}: batch {inp.batch}, seqlens U[{w['lengths'][0]},{w['lengths'][1]}], "
+                               f"s_q={w['s_q']}, h_q={w['h_q']}, h_kv={w['h_kv']}, d={w['d']}, page 64",
+                   "batch": inp.batch, "total_tokens": int(n.sum()), "seed": w["seed"]},
+        "mha_kernel_us_avg": round(ms * 1e3, 2),
+        "algorithmic_bytes": nbytes,
+        "algorithmic_flops": flops,
+        "kv_bytes_per_token": 2 * w["h_kv"] * w["d"] * 2,
+        "mla_kv_bytes_per_token": 1152,
+        "mla_algorithmic_bytes_same_sequences": mla_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": MI355X_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / MI355X_HBM_GBPS, 4),
+                     "traffic": cnt.get("bytes_per_call") if cnt else None},
+        "kernel_digest": kernel_digest("mha"),
+    }
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     """A plain device-to-device copy of known size, to calibrate the HBM
     byte counters (FETCH_SIZE / WRITE_SIZE) read by rocprofv3."""
@@ -649,7 +714,7 @@ def main():
                     help="one of %s, or 'all'; with --op kv_append one of %s or 'all'"
                          % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
     ap.add_argument("--op", default="decode",
-                    choices=("decode", "decode_fp8", "kv_append", "kv_append_fp8", "absorb"),
+                    choices=("decode", "decode_fp8", "kv_append", "kv_append_fp8", "absorb", "mha"),
                     help="decode (the hot path; default), decode over an FP8 latent cache (workloads "
                          "with h_q * s_q <= 64), the paged cache append, or the absorption products")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
@@ -693,6 +758,11 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.op == "mha":
+        names = list(MHA_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]
+        for name in names:
+            print(json.dumps(run_mha(name, args.steps, args.warmup)), flush=True)
         return
     if args.op == "absorb":
         names = list(ABSORB_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]

@@ -28,7 +28,7 @@ HEAD_DIM_V = 512
 PAGE_SIZE = 64
 FP8_PAGE_BYTES = 41216   # 64 x 512 E4M3 latent + 64 x 64 BF16 rotary + 64 FP32 scales
 
-__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "decode_fwd_fp8", "kv_append", "kv_append_fp8", "absorb_q", "absorb_o", "split_metadata_host",
+__all__ = ["SplitMeta", "get_split_metadata", "decode_fwd", "decode_fwd_fp8", "kv_append", "kv_append_fp8", "absorb_q", "absorb_o", "mha_decode_fwd", "split_metadata_host",
            "metadata_bytes", "workspace_bytes", "default_num_partitions", "MlaError"]
 
 
@@ -307,6 +307,39 @@ def absorb_o(o_lat: torch.Tensor, w_uv_t: torch.Tensor, out: Optional[torch.Tens
     check(lib().mla_absorb_o(o_lat.data_ptr(), w_uv_t.data_ptr(), tokens, h, d_v, out.data_ptr(),
                              _stream_ptr(dev)), "mla_absorb_o")
     return out
+
+
+def mha_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                   seqlens: torch.Tensor, softmax_scale: float, causal: bool,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Paged grouped-query MHA decode (mla_mha_decode_fwd), the contrast case.
+    q [B, s_q, h_q, 128]; k_cache, v_cache [num_pages, 64, h_kv, 128] bf16;
+    (h_q / h_kv) * s_q <= 16. Returns out [B, s_q, h_q, 128] bf16 and
+    lse [B, s_q, h_q] float32."""
+    dev = q.device
+    _require(q, "q", torch.bfloat16, ndim=4)
+    bsz, s_q, h_q, d = q.shape
+    if d != 128:
+        raise ValueError(f"q head dim must be 128, got {d}")
+    _require(k_cache, "k_cache", torch.bfloat16, device=dev, ndim=4)
+    _require(v_cache, "v_cache", torch.bfloat16, device=dev, ndim=4)
+    if k_cache.shape != v_cache.shape or k_cache.shape[1] != PAGE_SIZE or k_cache.shape[3] != 128:
+        raise ValueError("k_cache and v_cache must both be [num_pages, 64, h_kv, 128]")
+    h_kv = k_cache.shape[2]
+    _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
+    _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != bsz or seqlens.shape[0] != bsz:
+        raise ValueError("block_table and seqlens must have one row per sequence")
+    if out is None:
+        out = torch.empty((bsz, s_q, h_q, 128), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((bsz, s_q, h_q), dtype=torch.float32, device=dev)
+    check(lib().mla_mha_decode_fwd(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                   block_table.shape[1], seqlens.data_ptr(), bsz, s_q, h_q, h_kv,
+                                   k_cache.shape[0], ctypes.c_float(softmax_scale), int(bool(causal)),
+                                   out.data_ptr(), lse.data_ptr(), _stream_ptr(dev)), "mla_mha_decode_fwd")
+    return out, lse
 
 
 def timing_enable(enable: bool = True) -> None:

@@ -1,5 +1,6 @@
 """Loads libmla_decode.so and declares its C ABI (include/mla_decode.h,
-include/mla_decode_fp8.h, include/mla_kv_append.h, include/mla_absorb.h).
+include/mla_decode_fp8.h, include/mla_kv_append.h, include/mla_absorb.h,
+include/mla_mha.h).
 
 torch is imported first on purpose: torch ships its own HIP runtime with the
 same soname as /opt/rocm's, so loading the library after torch binds it to
@@ -38,6 +39,8 @@ SIGNATURES = {
     "mla_absorb_o": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_ptr, _c_ptr]),
     "mla_decode_fwd_fp8": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                     _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_mha_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                    _c_int, _c_float, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "mla_timing_enable": (_c_int, [_c_int]),
     "mla_timing_collect": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(_c_int)]),

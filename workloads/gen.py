@@ -376,11 +376,12 @@ def make_mha_inputs(seqlens: Sequence[int], s_q: int, h_q: int, h_kv: int, d: in
     return MhaInputs(base.seqlens, base.block_table, q, k, v, scale, bool(causal))
 
 
-# The contrast workload: the memory-bound decode step (64 sequences,
-# lengths U[3072, 5120], 16 query heads) under grouped-query MHA with 8 KV
-# heads of 128 values, the layout an MHA model of this size would cache.
+# The contrast workload: the memory-bound decode step under grouped-query
+# MHA with 8 KV heads of 128 values, the layout an MHA model of this size
+# would cache. Same seed and draw order as the memory-bound workload, so the
+# 64 sequence lengths (U[3072, 5120]) are exactly its lengths.
 MHA_WORKLOADS = {
-    "mha_memory_bound": dict(seed=25, batch=64, lengths=(3072, 5120), s_q=1, h_q=16, h_kv=8, d=128),
+    "mha_memory_bound": dict(seed=2, batch=64, lengths=(3072, 5120), s_q=1, h_q=16, h_kv=8, d=128),
 }
 
 
