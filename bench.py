@@ -192,7 +192,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     def step(i, ev=None):
         if ev is not None:
             ev[2].record(stream)
-        meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions)
+        meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions, fp8=fp8)
         if ev is not None:
             ev[0].record(stream)
         decode(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out,

@@ -42,10 +42,23 @@ extern "C" {
 #define MLA_FP8_PAGE_BYTES 41216
 
 /*
+ * mla_get_split_metadata_fp8 - the split plan for mla_decode_fwd_fp8.
+ *
+ * Same arguments, layout and semantics as mla_get_split_metadata. The FP8
+ * decode uses the 16-row kernels up to 64 rows, where the BF16 decode of a
+ * 64-row query block uses the 64-row kernel, so the two calls' plans differ
+ * there; mla_metadata_bytes and mla_workspace_bytes cover both.
+ */
+mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                      int num_partitions, int32_t* metadata, size_t metadata_bytes,
+                                      void* stream);
+
+/*
  * mla_decode_fwd_fp8 - mla_decode_fwd over FP8 pages.
  *
  *   kv_cache   device bytes [num_pages][MLA_FP8_PAGE_BYTES] in the layout
  *              above, 16-byte aligned
+ *   metadata   from mla_get_split_metadata_fp8 (or NULL: computed in-call)
  *   (all other arguments as for mla_decode_fwd)
  *
  * Supported: h_q * s_q <= 64 (the 16-row kernels); larger query blocks

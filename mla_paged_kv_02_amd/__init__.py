@@ -73,21 +73,24 @@ class SplitMeta:
     h_q: int
     s_q: int
     num_partitions: int
+    fp8: bool = False
 
 
 def get_split_metadata(seqlens: torch.Tensor, h_q: int, s_q: int,
-                       num_partitions: int = 0) -> SplitMeta:
-    """Build the split plan on the device, on the current stream."""
+                       num_partitions: int = 0, fp8: bool = False) -> SplitMeta:
+    """Build the split plan on the device, on the current stream; ``fp8``
+    builds the plan of decode_fwd_fp8 (mla_get_split_metadata_fp8)."""
     _require(seqlens, "seqlens", torch.int32, ndim=1)
     batch = seqlens.shape[0]
     nbytes = metadata_bytes(batch, h_q, s_q, num_partitions)
     if nbytes == 0:
         raise ValueError(f"unsupported shape batch={batch} h_q={h_q} s_q={s_q}")
     meta = torch.empty(nbytes // 4, dtype=torch.int32, device=seqlens.device)
-    check(lib().mla_get_split_metadata(seqlens.data_ptr(), batch, h_q, s_q, num_partitions,
-                                       meta.data_ptr(), nbytes, _stream_ptr(seqlens.device)),
-          "mla_get_split_metadata")
-    return SplitMeta(meta, batch, h_q, s_q, num_partitions)
+    fn = lib().mla_get_split_metadata_fp8 if fp8 else lib().mla_get_split_metadata
+    check(fn(seqlens.data_ptr(), batch, h_q, s_q, num_partitions, meta.data_ptr(), nbytes,
+             _stream_ptr(seqlens.device)),
+          "mla_get_split_metadata_fp8" if fp8 else "mla_get_split_metadata")
+    return SplitMeta(meta, batch, h_q, s_q, num_partitions, fp8)
 
 
 def split_metadata_host(seqlens, h_q: int, s_q: int, num_partitions: int) -> np.ndarray:
@@ -127,6 +130,8 @@ def decode_fwd(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tenso
             raise ValueError(f"kv_cache must be [num_pages, 64, 576], got {tuple(kv_cache.shape)}")
     else:
         raise ValueError("kv_cache must have 3 or 4 dims")
+    if meta is not None and meta.fp8:
+        raise ValueError("meta was built for decode_fwd_fp8 (fp8=True)")
     return _decode(lib().mla_decode_fwd, "mla_decode_fwd", q, kv_cache, block_table, seqlens, softmax_scale,
                    causal, meta, out, lse, workspace, num_partitions)
 
@@ -144,6 +149,8 @@ def decode_fwd_fp8(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.T
     _require(kv_pages, "kv_pages", torch.uint8, device=q.device, ndim=2)
     if kv_pages.shape[1] != FP8_PAGE_BYTES:
         raise ValueError(f"kv_pages must be [num_pages, {FP8_PAGE_BYTES}], got {tuple(kv_pages.shape)}")
+    if meta is not None and not meta.fp8:
+        raise ValueError("decode_fwd_fp8 needs the plan from get_split_metadata(..., fp8=True)")
     return _decode(lib().mla_decode_fwd_fp8, "mla_decode_fwd_fp8", q, kv_pages, block_table, seqlens,
                    softmax_scale, causal, meta, out, lse, workspace, num_partitions)
 

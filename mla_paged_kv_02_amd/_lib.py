@@ -29,6 +29,7 @@ SIGNATURES = {
     "mla_metadata_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "mla_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "mla_get_split_metadata": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "mla_get_split_metadata_fp8": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "mla_get_split_metadata_host": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size]),
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -97,7 +98,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 }  // namespace
 
-bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan) {
+bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan, bool fp8) {
     if (batch < 1 || h_q < 1 || s_q < 1) return false;
     const long long m = (long long)h_q * s_q;
     if (m > MLA_MAX_ROWS) return false;
@@ -108,8 +109,13 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.s_q = s_q;
     pl.M = (int)m;
     // Kernel choice (MLA_DECODE_KERNEL=rows16|ws overrides it): 16-row blocks
-    // while a sequence has at most 64 rows, 64-row blocks beyond.
-    DecodeKernel k = pl.M <= 64 ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
+    // below 64 rows, 64-row blocks from 64 rows on (at exactly 64 the 16-row
+    // kernel would stream every page four times, once per row block, and
+    // its per-CU load rate then bounds it: on the long-context workload the
+    // 64-row kernel is 15% faster despite its larger partials). The FP8
+    // cache has only the 16-row kernel: its plans take it up to 64 rows.
+    if (fp8 && pl.M > 64) return false;
+    DecodeKernel k = (pl.M < 64 || fp8) ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
     const int ov = kernel_override();
     if (ov >= 0) k = static_cast<DecodeKernel>(ov);
     const int tm = k == DecodeKernel::Rows16 ? 16 : 64;
@@ -184,20 +190,24 @@ int mla_default_num_partitions(int h_q, int s_q) {
     return pl.P;
 }
 
+// Sizes cover both the BF16 plan and, where one exists, the FP8 plan of the
+// same shape, so one buffer serves either decode call.
 size_t mla_metadata_bytes(int batch, int h_q, int s_q, int num_partitions) {
-    Plan pl;
-    if (!make_plan(batch, h_q, s_q, num_partitions,
-                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
-        return 0;
-    return metadata_bytes(pl);
+    const int cus = num_partitions > 0 ? 0 : current_cu_count();
+    Plan pl, pf;
+    if (!make_plan(batch, h_q, s_q, num_partitions, cus, &pl)) return 0;
+    size_t n = metadata_bytes(pl);
+    if (make_plan(batch, h_q, s_q, num_partitions, cus, &pf, true)) n = std::max(n, metadata_bytes(pf));
+    return n;
 }
 
 size_t mla_workspace_bytes(int batch, int h_q, int s_q, int num_partitions) {
-    Plan pl;
-    if (!make_plan(batch, h_q, s_q, num_partitions,
-                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
-        return 0;
-    return workspace_layout(pl, true).total;
+    const int cus = num_partitions > 0 ? 0 : current_cu_count();
+    Plan pl, pf;
+    if (!make_plan(batch, h_q, s_q, num_partitions, cus, &pl)) return 0;
+    size_t n = workspace_layout(pl, true).total;
+    if (make_plan(batch, h_q, s_q, num_partitions, cus, &pf, true)) n = std::max(n, workspace_layout(pf, true).total);
+    return n;
 }
 
 static mla_status check_meta_args(const int32_t* seqlens, int batch, int h_q, int s_q,
@@ -209,20 +219,31 @@ static mla_status check_meta_args(const int32_t* seqlens, int batch, int h_q, in
     return MLA_OK;
 }
 
-mla_status mla_get_split_metadata(const int32_t* seqlens, int batch, int h_q, int s_q,
-                                  int num_partitions, int32_t* metadata, size_t metadata_bytes_,
-                                  void* stream) {
+static mla_status get_split_metadata(const int32_t* seqlens, int batch, int h_q, int s_q, int num_partitions,
+                                     int32_t* metadata, size_t metadata_bytes_, void* stream, bool fp8) {
     mla_status st = check_meta_args(seqlens, batch, h_q, s_q, num_partitions, metadata);
     if (st != MLA_OK) return st;
     Plan pl;
     if (!make_plan(batch, h_q, s_q, num_partitions,
-                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl, fp8))
         return MLA_ERR_UNSUPPORTED;
     if (metadata_bytes_ < metadata_bytes(pl)) return MLA_ERR_WORKSPACE_TOO_SMALL;
     if (launch_split_metadata(seqlens, batch, pl.P, pl.cseg, pl.R, metadata,
                               reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
         return MLA_ERR_HIP;
     return MLA_OK;
+}
+
+mla_status mla_get_split_metadata(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                  int num_partitions, int32_t* metadata, size_t metadata_bytes_,
+                                  void* stream) {
+    return get_split_metadata(seqlens, batch, h_q, s_q, num_partitions, metadata, metadata_bytes_, stream, false);
+}
+
+mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q, int s_q,
+                                      int num_partitions, int32_t* metadata, size_t metadata_bytes_,
+                                      void* stream) {
+    return get_split_metadata(seqlens, batch, h_q, s_q, num_partitions, metadata, metadata_bytes_, stream, true);
 }
 
 mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_q, int s_q,
@@ -268,7 +289,7 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
 
     Plan pl;
     if (!make_plan(batch, h_q, s_q, num_partitions,
-                   num_partitions > 0 ? 0 : current_cu_count(), &pl))
+                   num_partitions > 0 ? 0 : current_cu_count(), &pl, fp8))
         return MLA_ERR_UNSUPPORTED;
     if (fp8) {
         if (pl.kernel != DecodeKernel::Rows16) return MLA_ERR_UNSUPPORTED;

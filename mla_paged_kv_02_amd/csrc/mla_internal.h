@@ -28,7 +28,8 @@ struct Plan {
 };
 
 // Returns false for unsupported shapes. num_partitions <= 0 selects the default.
-bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan);
+// fp8: the plan of the FP8-cache decode (16-row kernel, at most 64 rows).
+bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Plan* plan, bool fp8 = false);
 
 // Byte layout of the workspace: [metadata (optional)] [partial lse] [partial O].
 struct WorkspaceLayout {

@@ -204,3 +204,21 @@ def test_append_fp8_argument_checks(kw, status):
     assert _lib.lib().mla_kv_append_fp8(args["new"], args["batch"], args["s_new"], args["seqlens"], args["bt"],
                                         args["maxb"], args["kv"], args["pages"], args["skipped"],
                                         args["stream"]) == status
+
+
+def test_fp8_metadata_argument_checks():
+    lib = _lib.lib()
+    assert lib.mla_get_split_metadata_fp8(None, 2, 16, 1, 64, FAKE, 1 << 20, None) == INVALID
+    assert lib.mla_get_split_metadata_fp8(FAKE, 2, 128, 1, 64, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.mla_get_split_metadata_fp8(FAKE, 2, 16, 1, 64, FAKE, 16, None) == TOO_SMALL
+
+
+def test_size_queries_cover_the_fp8_plan():
+    # at 64 rows the BF16 plan uses the 64-row kernel, the FP8 plan the
+    # 16-row one; one buffer must fit either, also for large batches
+    lib = _lib.lib()
+    for batch in (1, 64, 4096):
+        m = lib.mla_metadata_bytes(batch, 64, 1, 64)
+        w = lib.mla_workspace_bytes(batch, 64, 1, 64)
+        meta16 = 4 * (16 + 8 * 64 + 4 * batch + 4 * batch)      # P = 64, R = 4
+        assert m >= meta16 and w > 0

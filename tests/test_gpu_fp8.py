@@ -23,7 +23,7 @@ def _run(inp, codes, rope, scales, num_partitions=0, use_meta=True):
     pages = torch.from_numpy(pack_fp8_pages(codes, rope, scales)).cuda()
     bt = torch.from_numpy(inp.block_table).cuda()
     sl = torch.from_numpy(inp.seqlens).cuda()
-    meta = mla.get_split_metadata(sl, inp.h_q, inp.s_q, num_partitions) if use_meta else None
+    meta = mla.get_split_metadata(sl, inp.h_q, inp.s_q, num_partitions, fp8=True) if use_meta else None
     out, lse = mla.decode_fwd_fp8(q, pages, bt, sl, inp.scale, inp.causal, meta=meta,
                                   num_partitions=num_partitions)
     torch.cuda.synchronize()

@@ -121,7 +121,10 @@ def test_device_metadata_matches_host():
         host_parts = parts if parts > 0 else mla.default_num_partitions(h_q, s_q)
         host = mla.split_metadata_host(seqlens, h_q, s_q, host_parts)
         dev = meta.metadata.cpu().numpy()
-        assert np.array_equal(dev, host), f"device metadata differs for h_q={h_q} parts={parts}"
+        # the buffer is sized for either decode's plan; compare this plan's
+        # ints: header, 8 per partition, 4 per sequence, R counters per sequence
+        used = 16 + 8 * int(host[2]) + 4 * int(host[1]) + int(host[8]) * int(host[1])
+        assert np.array_equal(dev[:used], host[:used]), f"device metadata differs for h_q={h_q} parts={parts}"
     # more sequences than the scheduler keeps in LDS, and cost lines long
     # enough that partition arithmetic needs more than 32 bits
     for batch, top, parts in [(9000, 3000, 4096), (64, 1 << 24, 60000), (3, 1 << 26, 65536)]:
