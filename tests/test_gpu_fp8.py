@@ -201,3 +201,30 @@ def test_fp8_append_full_size():
     from workloads import make_append_workload
     inp = make_append_workload("append_prefill_chunk")
     _append_fp8_case(inp, "append_prefill_chunk")
+
+
+def test_fp8_pages_past_4_gib():
+    """FP8 pages at the top of a 4.3 GB page buffer (offsets past 2^32 bytes):
+    decode against the oracle on the same logical content."""
+    import torch
+    inp = make_inputs([300, 70, 129], 1, 16, seed=93)
+    codes, rope, scales = make_fp8_cache(inp, seed=94)
+    nb = inp.num_pages
+    total = 105000                                  # 105000 * 41216 B = 4.3 GB
+    shift = total - nb
+    log(f"[case] fp8 pages past 4 GiB: {total} pages, used at {shift}..")
+    big = torch.empty((total, FP8_PAGE_BYTES), dtype=torch.uint8, device="cuda")
+    big[shift:] = torch.from_numpy(pack_fp8_pages(codes, rope, scales)).cuda()
+    table = np.where(inp.block_table >= 0, inp.block_table + shift, -1).astype(np.int32)
+    import mla_paged_kv_02_amd as mla
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out, lse = mla.decode_fwd_fp8(q, big, torch.from_numpy(table).cuda(), torch.from_numpy(inp.seqlens).cuda(),
+                                  inp.scale, False)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.mla_decode_fp8_ref(inp.q_bits, codes, rope, scales, inp.block_table, inp.seqlens,
+                                                 inp.scale, False)
+    s = score(out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref_out, ref_lse)
+    log(f"  {s}")
+    assert s.ok(), str(s)
+    del big
+    torch.cuda.empty_cache()

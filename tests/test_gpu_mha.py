@@ -85,3 +85,30 @@ def test_mha_rejects_groups_over_16_rows():
     with pytest.raises(mla.MlaError, match="UNSUPPORTED"):
         mla.mha_decode_fwd(dev(inp.q_bits), dev(inp.k_bits), dev(inp.v_bits), torch.from_numpy(inp.block_table).cuda(),
                            torch.from_numpy(inp.seqlens).cuda(), inp.scale, False)
+
+
+def test_mha_pages_past_4_gib():
+    """Key and value pages at the top of 4.3 GB caches (offsets past 2^32)."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    inp = make_mha_inputs([300, 70, 129], 1, 16, 8, 128, seed=530)
+    nb = inp.k_bits.shape[0]
+    total = 33000                                   # 33000 * 131072 B = 4.3 GB each
+    shift = total - nb
+    log(f"[case] mha pages past 4 GiB: {total} pages, used at {shift}..")
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    k = torch.empty((total, 64, 8, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    k[shift:] = dev(inp.k_bits)
+    v[shift:] = dev(inp.v_bits)
+    table = np.where(inp.block_table >= 0, inp.block_table + shift, -1).astype(np.int32)
+    out, lse = mla.mha_decode_fwd(dev(inp.q_bits), k, v, torch.from_numpy(table).cuda(),
+                                  torch.from_numpy(inp.seqlens).cuda(), inp.scale, False)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.mha_decode_ref(inp.q_bits, inp.k_bits, inp.v_bits, inp.block_table, inp.seqlens,
+                                             inp.scale, False)
+    s = score(out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref_out, ref_lse)
+    log(f"  {s}")
+    assert s.ok(), str(s)
+    del k, v
+    torch.cuda.empty_cache()

@@ -220,3 +220,41 @@ def test_reference_restart_on_dominant_key(h_q, s_q, causal, parts):
     inp = _with_dominant_keys(inp, [(0, 2500), (1, 600), (2, 100)])
     out, lse = _check(inp, num_partitions=parts, tag=f"restart h_q={h_q} parts={parts}")
     assert np.all(np.isfinite(lse))
+
+
+def test_pages_past_4_gib():
+    """A 5.3 GB cache with the used pages at its top: page offsets pass 2^32
+    bytes, so 32-bit address arithmetic anywhere would read the wrong rows.
+    Decode, and the cache append into those pages, against the oracle on the
+    same logical content."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from workloads import make_append_inputs
+    inp = make_inputs([300, 70, 129], 2, 16, seed=91, causal=True)
+    nb = inp.num_pages
+    total = 72000                                       # 72000 * 73728 B = 5.3 GB
+    shift = total - nb
+    log(f"[case] pages past 4 GiB: cache {total} pages, used pages at {shift}..{total - 1}")
+    big = torch.empty((total, 64, 1, 576), dtype=torch.bfloat16, device="cuda")
+    big[shift:] = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    table = np.where(inp.block_table >= 0, inp.block_table + shift, -1).astype(np.int32)
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.from_numpy(inp.seqlens).cuda()
+    out, lse = mla.decode_fwd(q, big, bt, sl, inp.scale, True)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens,
+                                             inp.scale, True)
+    s = score(out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy(), ref_out, ref_lse)
+    log(f"  decode {s}")
+    assert s.ok(), str(s)
+    # append two new tokens per sequence into the top pages
+    app = make_append_inputs([300, 70, 129], 2, seed=92)
+    new = torch.from_numpy(app.new_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    mla.kv_append(new, sl, bt, big)
+    torch.cuda.synchronize()
+    ref_kv, _ = oracle.kv_append_ref(inp.kv_bits, app.new_bits, inp.block_table, inp.seqlens)
+    got = big[shift:].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, ref_kv), "append into pages past 4 GiB"
+    del big
+    torch.cuda.empty_cache()
