@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     // (every batch up to kLdsBatch sequences); larger batches search the copy
     // in the metadata itself
     __shared__ int32_t s_start[kLdsBatch];
-    __shared__ int32_t s_pages[kLdsBatch];
+    __shared__ int32_t s_len[kLdsBatch];   // lengths, so no record waits on a second global read
     __shared__ int wave_sums[4][kSchedThreads / 64];   // scan totals, by call
     const bool in_lds = batch <= kLdsBatch;
     int32_t* seq = meta + kMetaHeader + kPartInts * P;
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
             seq[4 * b + 3] = carry + ex;
             if (in_lds) {
                 s_start[b] = carry + ex;
-                s_pages[b] = pages_of(len);
+                s_len[b] = len;
             }
         }
         carry += chunk_total;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
         if (b < batch) {
             // both written by this thread above
             const int32_t st = in_lds ? s_start[b] : seq[4 * b + 3];
-            const int32_t np = in_lds ? s_pages[b] : pages_of(seqlens[b]);
+            const int32_t np = pages_of(in_lds ? s_len[b] : seqlens[b]);
             if (np > 0) {   // seq_partitions with the divisions above
                 first = (int32_t)floor_div((int64_t)(st + cseg + 1) * pa - 1, total);
                 const int32_t z = (int32_t)floor_div((int64_t)(st + cseg + np) * pa - 1, total);
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
             bound(floor_div((int64_t)p * total, pa), &v[0], &v[1]);
             bound(floor_div((int64_t)(p + 1) * total, pa), &v[2], &v[3]);
             e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
-            e[4] = v[0] < batch ? seqlens[v[0]] : 0;
+            e[4] = v[0] < batch ? (in_lds ? s_len[v[0]] : seqlens[v[0]]) : 0;
         } else {
             e[0] = batch; e[1] = 0; e[2] = batch; e[3] = 0;
             e[4] = 0;
