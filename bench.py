@@ -128,17 +128,10 @@ def streaming_context(nbytes: int = 1 << 30, reps: int = 10):
             "torch_copy_gbps": round(2 * nbytes / t_copy / 1e9, 1)}
 
 
-def cpu_baseline(workload: str, inp, budget_s: float):
-    """The FP64 oracle, untuned, on a bounded sample of the same workload:
-    whole sequences in order, wrapping round the batch, until ~budget_s of
-    wall time. Reported in the workload's algorithmic GB/s."""
+def _oracle_sample(inp, budget_s: float):
+    """Whole sequences through the oracle, in order and wrapping round the
+    batch, until ~budget_s of wall time: (sequence indices, seconds)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    w = WORKLOADS[workload]
     t0 = time.perf_counter()
     done = []
     while True:
@@ -148,17 +141,37 @@ def cpu_baseline(workload: str, inp, budget_s: float):
         done.append(b)
         if time.perf_counter() - t0 >= budget_s:
             break
-    dt = time.perf_counter() - t0
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(workload: str, inp, budget_s: float):
+    """The FP64 oracle, untuned, on a bounded sample of the same workload,
+    with the BLAS threads the host gives it and again with one thread (a
+    third of the budget). Reported in the workload's algorithmic GB/s."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads, threadpool_limits = 1, None
+    w = WORKLOADS[workload]
+    done, dt = _oracle_sample(inp, budget_s)
     nbytes = algorithmic_bytes(inp.seqlens[done], w.s_q, w.h_q)
     passes = len(done) / inp.batch
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {inp.batch}-sequence "
-                      f"batch, {int(inp.seqlens[done].sum())} tokens) in {dt:.1f} s; numpy FP64 "
-                      f"two-pass softmax per sequence, GB/s from the same algorithmic-bytes formula",
-            "seconds": round(dt, 2),
-            "cpu_model": cpu_model(),
-            "host_cpus": len(os.sched_getaffinity(0))}
+    res = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{len(done)} sequence decodes ({passes:.2f} passes over the {inp.batch}-sequence "
+                     f"batch, {int(inp.seqlens[done].sum())} tokens) in {dt:.1f} s; numpy FP64 "
+                     f"two-pass softmax per sequence, GB/s from the same algorithmic-bytes formula",
+           "seconds": round(dt, 2),
+           "cpu_model": cpu_model(),
+           "host_cpus": len(os.sched_getaffinity(0))}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            done1, dt1 = _oracle_sample(inp, budget_s / 3)
+        res["single_thread"] = {"value": round(algorithmic_bytes(inp.seqlens[done1], w.s_q, w.h_q) / dt1 / 1e9, 4),
+                                "unit": "GB/s", "cores": 1, "sequences": len(done1),
+                                "seconds": round(dt1, 2)}
+    return res
 
 
 def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_bytes: int,
