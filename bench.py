@@ -171,6 +171,13 @@ def cpu_baseline(workload: str, inp, budget_s: float):
         res["single_thread"] = {"value": round(algorithmic_bytes(inp.seqlens[done1], w.s_q, w.h_q) / dt1 / 1e9, 4),
                                 "unit": "GB/s", "cores": 1, "sequences": len(done1),
                                 "seconds": round(dt1, 2)}
+    # the pure-Python definition (exactly rounded sums) on the tiny decode only
+    import oracle
+    tiny = make_workload_inputs("tiny")
+    t0 = time.perf_counter()
+    oracle.mla_decode_bruteforce(oracle.bf16_bits_to_f64(tiny.q_bits), oracle.bf16_bits_to_f64(tiny.kv_bits),
+                                 tiny.block_table, tiny.seqlens, tiny.scale, tiny.causal)
+    res["bruteforce_tiny_seconds"] = round(time.perf_counter() - t0, 3)
     return res
 
 
