@@ -126,6 +126,12 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     if (p <= 0) {
         const int cus = num_cus > 0 ? num_cus : 256;
         p = cus / pl.R;
+        // A single 64-row block per partition: three partitions per four
+        // CUs. The stream still fills HBM (each workgroup could take a third
+        // more than its share), and a quarter fewer 128 KB FP32 partials
+        // shortens the combine (4 sequences of 1K-64K tokens at 64 heads:
+        // call 53.4 vs 55.5 us, decode kernel unchanged).
+        if (k == DecodeKernel::WaveSplit && pl.R == 1) p = cus * 3 / 4;
         if (p < 1) p = 1;
     }
     pl.P = (p + 7) / 8 * 8;  // whole groups of 8 for the XCD-aware block mapping
