@@ -100,18 +100,20 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
 #pragma unroll
     for (int u = 0; u < kCombineUnroll; ++u)
         if (sub + u * kWPI < cnt) accumulate(x[u], wt[u]);
-    int s = sub + kCombineUnroll * kWPI;
-    for (; s + (kCombineUnroll - 1) * kWPI < cnt; s += kCombineUnroll * kWPI) {
+    // further groups, a partly filled last one included: one round trip each
+    for (int s = sub + kCombineUnroll * kWPI; s < cnt; s += kCombineUnroll * kWPI) {
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
-            x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)(s + u * kWPI) * pstride);
-            wt[u] = ld_const_f32(lp, s + u * kWPI);
+            const int su = s + u * kWPI;
+            if (su < cnt) {
+                x[u] = *reinterpret_cast<const f32x4*>(pbase + (size_t)su * pstride);
+                wt[u] = ld_const_f32(lp, su);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) accumulate(x[u], wt[u]);
+        for (int u = 0; u < kCombineUnroll; ++u)
+            if (s + u * kWPI < cnt) accumulate(x[u], wt[u]);
     }
-    for (; s < cnt; s += kWPI) accumulate(*reinterpret_cast<const f32x4*>(pbase + (size_t)s * pstride),
-                                          ld_const_f32(lp, s));
     if constexpr (kWPI > 1) {
         red[w][lane] = acc;
         __syncthreads();
@@ -133,15 +135,17 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
 
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
     // Partials per split sequence average about P / batch + 1; the waves
-    // sharing an item grow with that figure.
+    // sharing an item grow with that figure, so that a wave's share of an
+    // item (its partials s = sub, sub + waves, ...) usually fits in the one
+    // group of loads issued before the lse reduction.
     // Consecutive blocks go to different XCDs, and a sequence's blocks are
     // consecutive, so a long sequence's work spreads over all of them.
     const int per_seq = plan.P / plan.batch;
     const int items = 2 * plan.M;
     const unsigned nb = (unsigned)plan.batch;
-    if (per_seq >= 64) {
+    if (per_seq >= 4 * kCombineUnroll) {
         hipLaunchKernelGGL(mla_combine_kernel<16>, dim3(nb * items), dim3(64 * 16), 0, stream, args);
-    } else if (per_seq >= 16) {
+    } else if (per_seq >= kCombineUnroll) {
         hipLaunchKernelGGL(mla_combine_kernel<4>, dim3(nb * items), dim3(64 * 4), 0, stream, args);
     } else {
         hipLaunchKernelGGL(mla_combine_kernel<1>, dim3(nb * ((items + 3) / 4)), dim3(64 * 4), 0, stream, args);
