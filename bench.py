@@ -773,7 +773,7 @@ def main():
         ingest_mfma(args.workload, args.kernel, args.ingest_mfma, command=args.command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1",
+        print("bench.py: the decode library runs on one GPU (it has no multi-GPU path); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
