@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void mla_decode_rows16_fp8_kernel(DecodeArgs a
                 if (wave == 0 && g == 0) a.lse[(size_t)b * a.M + row] = lse_v;
             } else {
                 float* pp = a.part_o + ((size_t)slotno * a.M + row) * kHeadDimV + col0;
-                TileStores<8>::part(pp, res);
+                TileStores<8>::part(pp, res, a.counters != nullptr);
                 if (wave == 0 && g == 0)
                     __hip_atomic_store(&a.part_lse[(size_t)row * a.lse_stride + slotno], lse_v, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);

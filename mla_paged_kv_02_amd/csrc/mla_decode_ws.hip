@@ -487,7 +487,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                             v[t] = o[rt][t];
                             v[t][0] *= inv; v[t][1] *= inv; v[t][2] *= inv; v[t][3] *= inv;
                         }
-                        TileStores<kVTiles>::part(pp, v);
+                        TileStores<kVTiles>::part(pp, v, a.counters != nullptr);
                     }
                 }
             }
