@@ -140,12 +140,15 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.cseg = 1 + tm / 16;
     pl.slots = 2 * pl.P;
     // With no more partitions than sequences most sequences sit in one
-    // partition and the few split ones have about two partials: the merge
-    // then runs in the decode kernel and the call is one kernel. With more
-    // partitions per sequence the merging workgroups' extra reads land on
-    // the critical path, and a combine kernel spreads them instead
+    // partition and the few split ones have about two partials: below 128
+    // rows the merge then runs in the decode kernel and the call is one
+    // kernel. With more partitions per sequence the merging workgroups'
+    // extra reads land on the critical path, and from 128 rows the partials
+    // are large enough that writing them through to the coherent level costs
+    // more than a second kernel (128 heads, 128 sequences of 4096 tokens:
+    // call 186-190 vs 192-195 us); a combine kernel merges them instead
     // (MLA_COMBINE=kernel|fused, read at every call, overrides the choice).
-    pl.fused_combine = pl.P <= pl.batch;
+    pl.fused_combine = pl.P <= pl.batch && pl.M < 128;
     if (const char* e = std::getenv("MLA_COMBINE")) {
         if (!std::strcmp(e, "kernel")) pl.fused_combine = false;
         if (!std::strcmp(e, "fused")) pl.fused_combine = true;
