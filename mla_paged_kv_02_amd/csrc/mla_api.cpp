@@ -286,7 +286,10 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
     if (batch < 1 || s_q < 1 || h_q < 1 || max_blocks_per_seq < 1 || num_pages < 1)
         return MLA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
-    if (!std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
+    // the kernels take the row maximum of raw scores and scale it, which is
+    // the maximum of the scaled scores only for a positive scale; -0.0 and
+    // NaN fail this test too
+    if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return MLA_ERR_INVALID_ARG;
     if (num_partitions > 65536) return MLA_ERR_INVALID_ARG;
     if ((long long)h_q * s_q > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
     if ((long long)max_blocks_per_seq * batch > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;

@@ -214,7 +214,6 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 
             int L[NR];
             float m_ref[NR], l_run[NR];
-            const float inv_scale = 1.f / a.scale_log2;
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 L[r] = a.causal ? min(max(nseq - a.s_q + stok[r] + 1, 0), nseq) : nseq;
@@ -338,13 +337,17 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                                 if (m_ref[r] == -INFINITY) m_ref[r] = mx == -INFINITY ? -INFINITY : mx + kRefMargin;
                             }
                         }
-                        // overflow: a score above the reference plus the
-                        // headroom, tested on raw scores against the limit
-                        // divided back by the scale (a bound, not a rounding
-                        // decision: weights stay below 2^64 either way)
+                        // overflow: a scaled score above the reference plus
+                        // the headroom. The lane's maximum times the scale is
+                        // the maximum of its scaled scores (scale > 0, and
+                        // rounding is monotonic), and the row maximum is at
+                        // least the lane's, so a lane that reports overflow
+                        // always raises its row's reference: every restart
+                        // strictly raises some reference to a score of the
+                        // segment plus the margin, and the restarts end.
                         bool over = false;
 #pragma unroll
-                        for (int r = 0; r < NR; ++r) over = over || (lm[r] > (m_ref[r] + kHeadroom) * inv_scale);
+                        for (int r = 0; r < NR; ++r) over = over || (lm[r] * a.scale_log2 > m_ref[r] + kHeadroom);
                         if (__ballot(over) != 0) {
 #pragma unroll
                             for (int r = 0; r < NR; ++r) {

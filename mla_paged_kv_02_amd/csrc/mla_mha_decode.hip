@@ -236,8 +236,8 @@ extern "C" mla_status mla_mha_decode_fwd(const void* q, const void* k_cache, con
     if (batch < 1 || s_q < 1 || h_q < 1 || h_kv < 1 || max_blocks_per_seq < 1 || num_pages < 1)
         return MLA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return MLA_ERR_INVALID_ARG;
-    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
-        return MLA_ERR_INVALID_ARG;
+    // finite and > 0, the contract shared with mla_decode_fwd (NaN and -0.0 fail it)
+    if (!(softmax_scale > 0.f) || softmax_scale > 3.4028235e38f) return MLA_ERR_INVALID_ARG;
     if (h_q % h_kv) return MLA_ERR_INVALID_ARG;
     if ((h_q / h_kv) * s_q > 16) return MLA_ERR_UNSUPPORTED;
     if ((long long)batch * h_kv > 0x7fffffffLL || (long long)max_blocks_per_seq * batch > (1LL << 31) - 1 ||

@@ -78,6 +78,10 @@ def _decode(**kw):
     (dict(h_q=0), INVALID), (dict(maxb=0), INVALID), (dict(pages=0), INVALID),
     (dict(causal=2), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(nparts=70000), INVALID),
+    # the contract is scale > 0: the kernels scale the raw row maximum, which
+    # is the maximum of the scaled scores only for a positive scale
+    (dict(scale=-1.0), INVALID), (dict(scale=-0.0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=-float("inf")), INVALID),
     (dict(h_q=128, s_q=16), UNSUPPORTED),
     (dict(q=FAKE + 8), MISALIGNED), (dict(kv=FAKE + 4), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
     (dict(ws=FAKE + 8), MISALIGNED), (dict(bt=FAKE + 2), MISALIGNED), (dict(lse=FAKE + 1), MISALIGNED),
@@ -185,6 +189,8 @@ def _decode_fp8(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(kv=None), INVALID), (dict(q=None), INVALID), (dict(batch=0), INVALID), (dict(causal=3), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=-0.0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(h_q=128), UNSUPPORTED), (dict(h_q=16, s_q=8), UNSUPPORTED),
     (dict(kv=FAKE + 4), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED), (dict(ws_bytes=1024), TOO_SMALL),
 ])
@@ -222,3 +228,24 @@ def test_size_queries_cover_the_fp8_plan():
         w = lib.mla_workspace_bytes(batch, 64, 1, 64)
         meta16 = 4 * (16 + 8 * 64 + 4 * batch + 4 * batch)      # P = 64, R = 4
         assert m >= meta16 and w > 0
+
+
+def _mha(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxb=4, seqlens=FAKE, batch=2, s_q=1, h_q=16, h_kv=8,
+                pages=8, scale=1 / 24, causal=0, out=FAKE, lse=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_mha_decode_fwd(
+        args["q"], args["k"], args["v"], args["bt"], args["maxb"], args["seqlens"], args["batch"],
+        args["s_q"], args["h_q"], args["h_kv"], args["pages"], ctypes.c_float(args["scale"]),
+        args["causal"], args["out"], args["lse"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(h_kv=0), INVALID),
+    (dict(h_q=12, h_kv=8), INVALID), (dict(causal=2), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(scale=-0.0), INVALID), (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(h_q=64, h_kv=2), UNSUPPORTED), (dict(q=FAKE + 8), MISALIGNED), (dict(out=FAKE + 4), MISALIGNED),
+])
+def test_mha_argument_checks(kw, status):
+    assert _mha(**kw) == status
