@@ -68,10 +68,15 @@ mla_status mla_kv_append(const void* new_rows, int batch, int s_new, const int32
  * with one FP32 scale, its 64 rotary values copied as BF16, and the scale
  * stored in its group. Quantisation of a row x (BF16 values, exact in FP32):
  *
- *   scale = fl32(amax / 448) (amax = max |x_d|; 1 for an all-zero row)
- *   y_d   = fl32(x_d / scale)
- *   byte  = the E4M3 value nearest |y_d|, ties to the even mantissa,
- *           magnitudes past 448 saturating to 448; sign bit of y_d
+ *   scale = fl32(amax / 448), the FP32 number nearest amax / 448
+ *           (amax = max |x_d|; 1 for an all-zero row)
+ *   byte  = the E4M3 value nearest the exact quotient |x_d| / scale, ties
+ *           to the even mantissa, magnitudes past 448 saturating to 448;
+ *           sign bit of x_d
+ *
+ * (the exact quotient, not its FP32 rounding: where fl32(x_d / scale) lands
+ * on a midpoint between two E4M3 values the exact quotient usually does
+ * not, and the nearer value is the one on its side)
  *
  * Arguments as for mla_kv_append, with kv_pages device bytes
  * [num_pages][MLA_FP8_PAGE_BYTES], 16-byte aligned, in place of kv_cache.

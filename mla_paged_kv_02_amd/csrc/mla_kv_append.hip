@@ -84,13 +84,20 @@ __global__ __launch_bounds__(kAppendThreads) void mla_kv_append_kernel(AppendArg
 //
 // One wave per new token: lane l holds latent values 8l..8l+7 (16 bytes of
 // the BF16 row), lanes 0..7 also its rotary chunk l. The row's largest
-// magnitude comes from a wave reduction; scale = amax / 448 and
-// y = x / scale are FP32 divisions (correctly rounded), and y is rounded to
-// E4M3 in integer arithmetic: magnitudes at or past 448 saturate to 448;
-// below 2^-6 the code is rint(|y| * 2^9) (subnormal steps of 2^-9); above,
-// |y| * 2^(3 - e) lies in [8, 16) for e = floor(log2 |y|) and rint of it
-// gives the mantissa (a carry to 16 moves to the next binade by itself:
-// code = 8 (e + 7) + r - 8). rint rounds half to even; the sign bit is y's.
+// magnitude comes from a wave reduction and scale = amax / 448 is an FP32
+// division (correctly rounded: the stored scale is the FP32 number nearest
+// amax / 448). Each code is the E4M3 value nearest the exact quotient
+// |x| / scale, ties to the even mantissa: y = fl32(x / scale) is rounded to
+// E4M3 in integer arithmetic (magnitudes at or past 448 saturate to 448;
+// below 2^-6 the code is rint(|y| * 2^9), subnormal steps of 2^-9; above,
+// |y| * 2^(3 - e) lies in [8, 16) for e = floor(log2 |y|) and its rounding
+// gives the mantissa, a carry to 16 moving to the next binade by itself:
+// code = 8 (e + 7) + r - 8). Only where y lands exactly on a midpoint can
+// the exact quotient lie on the other side of it than y suggests; there
+// the sign of the residual |x| - |y| * scale, computed exactly by one FMA,
+// says which side (zero: an exact midpoint, ties to even). Rounding is
+// monotonic, so a y off a midpoint is on the same side as the exact
+// quotient. The sign bit is x's.
 constexpr int kAppendF8Threads = 256;   // four tokens per workgroup
 
 struct AppendF8Args {
@@ -102,17 +109,35 @@ struct AppendF8Args {
     int batch, s_new, max_blocks, num_pages, tokens;
 };
 
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
+// t = |y| in grid-step units (the mantissa position, or |y| * 2^9 below
+// 2^-6): rounded to nearest, a half-way t decided by the residual's sign.
+__device__ __forceinline__ float round_grid(float t, float resid) {
+    const float fl = floorf(t);
+    if (t - fl != 0.5f) return rintf(t);
+    if (resid > 0.f) return fl + 1.f;
+    if (resid < 0.f) return fl;
+    return rintf(t);   // an exact midpoint: even
+}
+
+__device__ __forceinline__ uint32_t e4m3_code(float x, float scale) {
+    const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    const float a = fabsf(x / scale);
+    const float ax = fabsf(x);
+    // |x| - a * scale exactly: a at a midpoint has at most five significant
+    // bits and the product at most 29, so one FMA rounds the exact residual
+    // only where it would fall below the FP32 range; for |x| < 2^-60 both
+    // operands are first scaled by 2^64 (exact) so that it never does
+    const float up = ax < 0x1p-60f ? 0x1p64f : 1.f;
     uint32_t mag;
     if (!(a < 448.f)) {
         mag = 0x7Eu;
     } else if (a < 0x1p-6f) {
-        mag = (uint32_t)rintf(a * 0x1p9f);
+        const float t = a * 0x1p9f;
+        mag = (uint32_t)round_grid(t, t - floorf(t) == 0.5f ? fmaf(-a, scale * up, ax * up) : 0.f);
     } else {
         const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;    // -6 .. 8
-        const float r = rintf(ldexpf(a, 3 - e));                          // 8 .. 16
+        const float t = ldexpf(a, 3 - e);                                 // 8 .. 16
+        const float r = round_grid(t, t - floorf(t) == 0.5f ? fmaf(-a, scale * up, ax * up) : 0.f);
         mag = (uint32_t)(8 * (e + 7) + (int)r - 8);
         mag = mag > 0x7Eu ? 0x7Eu : mag;
     }
@@ -149,9 +174,9 @@ __global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(App
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k] / scale) << (8 * k);
+    for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k], scale) << (8 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k] / scale) << (8 * k);
+    for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k], scale) << (8 * k);
     const int slot = p & (kPageRows - 1);
     uint8_t* grp = a.pages + (size_t)page * MLA_FP8_PAGE_BYTES + (slot >> 4) * (MLA_FP8_PAGE_BYTES / 4);
     const int r = slot & 15;

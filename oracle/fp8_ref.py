@@ -20,11 +20,13 @@ Readings where the pages leave it open:
 * Decode over this cache is decode over the dequantised rows: every formula
   of the BF16 reference applies unchanged to the rows
   [decode(bytes) * scale ; rope].
-* The quantiser (the cache writer's rule) takes scale = amax / 448 over the
-  token's 512 values (zero rows get scale 1) and rounds x / scale to the
-  nearest E4M3 value, ties to the even mantissa, saturating at 448; the
-  scale and the quotient are FP32 operations, as in the kernel that writes
-  the cache.
+* The quantiser (the cache writer's rule) stores one FP32 scale per token,
+  the FP32 number nearest amax / 448 over the token's 512 values (zero rows
+  get scale 1), and codes each value as the E4M3 value nearest the exact
+  quotient x / scale, ties to the even mantissa, saturating at 448. That is
+  the format's round-to-nearest applied to the real number the stored
+  scale and the input define; no intermediate rounding of the quotient
+  enters the definition.
 """
 
 from __future__ import annotations
@@ -62,28 +64,34 @@ def quantize_e4m3_rows(rows: np.ndarray):
     """rows [N, 512] (values exact in float32, e.g. BF16 inputs) ->
     (codes uint8 [N, 512], scale float32 [N]).
 
-    Every step is taken in FP32, as a kernel writing the cache would take it
-    (a quantised code is an integer decided by floating point, so both sides
-    decide it in the same precision): scale = fl32(amax / 448) per row (1 for
-    an all-zero row), y = fl32(x / scale), then y is rounded to the nearest
-    E4M3 value, ties to the even mantissa, magnitudes above 448 saturating
-    to 448. The sign bit is y's (so a negative value that rounds to zero is
-    0x80, negative zero)."""
+    The scale is stored as an FP32 number: scale = fl32(amax / 448), the
+    FP32 value nearest the row's largest magnitude over 448 (1 for an
+    all-zero row). Each value's code is the E4M3 value nearest the exact
+    quotient |x| / scale, ties to the even mantissa, magnitudes past 448
+    saturating to 448; the sign bit is x's (a negative value that rounds to
+    zero gives 0x80, negative zero).
+
+    The nearest grid value is found by counting the midpoints between
+    neighbouring grid values that lie strictly below the quotient; a
+    quotient exactly at a midpoint takes the even code of the two. Each
+    comparison |x| > mid * scale is exact in float64: mid has at most five
+    significant bits and scale 24, so their product is a float64 number."""
     x = np.asarray(rows, dtype=np.float32)
     amax = np.abs(x).max(axis=1)
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    y = (x / scale[:, None]).astype(np.float32)
-    mag = np.abs(y).astype(np.float64)
     grid = _E4M3_TABLE[:0x7F]                      # codes 0x00..0x7E, increasing
-    idx = np.clip(np.searchsorted(grid, mag), 1, grid.size - 1)
-    lo, hi = grid[idx - 1], grid[idx]
-    pick_hi = (hi - mag) < (mag - lo)
-    tie = (hi - mag) == (mag - lo)
-    pick_hi = pick_hi | (tie & (idx % 2 == 0))     # code idx is even
-    code = np.where(pick_hi, idx, idx - 1)
-    code = np.where(mag >= grid[-1], 0x7E, code)
-    code = np.where(mag <= 0.0, 0, code)
-    neg = np.signbit(y)
+    mids = (grid[:-1] + grid[1:]) / 2              # 126 midpoints, exact in float64
+    odd = (np.arange(mids.size) % 2) == 1          # midpoint k lies between codes k and k + 1
+    mag = np.abs(x).astype(np.float64)
+    code = np.empty(x.shape, dtype=np.int64)
+    for r in range(x.shape[0]):
+        bounds = mids * float(scale[r])            # exact products, increasing
+        below = np.searchsorted(bounds, mag[r], side="left")   # midpoints strictly below
+        at = np.zeros(mag.shape[1], dtype=bool)
+        inside = below < bounds.size
+        at[inside] = bounds[below[inside]] == mag[r, inside]
+        code[r] = below + (at & odd[np.minimum(below, bounds.size - 1)])
+    neg = np.signbit(x)
     return (code | np.where(neg, 0x80, 0)).astype(np.uint8), scale
 
 

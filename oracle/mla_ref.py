@@ -80,28 +80,27 @@ def attend_rows(q: np.ndarray, k: np.ndarray, lengths: Sequence[int], scale: flo
     q: [R, 576]; k: [N, 576] (values are k[:, :512]); lengths[r] keys are
     visible to row r. Returns out [R, 512], lse [R] (float64).
 
-    Pass 1 scores every visible key, s_t = scale * <q, k_t>, and reduces them
-    to the log-sum-exp. Pass 2 weights the value rows by exp(s_t - lse).
+    Rows that see the same keys (the same length L) are taken together.
+    Pass 1 scores their visible keys, s_t = scale * <q, k_t> for t < L, and
+    reduces each row to its log-sum-exp. Pass 2 weights the value rows by
+    exp(s_t - lse) and sums them.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     r_count = q.shape[0]
     out = np.zeros((r_count, D_V), dtype=np.float64)
     lse = np.full(r_count, -np.inf, dtype=np.float64)
-    if k.shape[0] == 0:
-        return out, lse
-    scores = scale * (q @ k.T)                     # [R, N]
-    values = k[:, :D_V]                            # [N, 512]
-    for r in range(r_count):
-        L = int(lengths[r])
+    lengths = np.asarray(lengths, dtype=np.int64).reshape(r_count)
+    for L in np.unique(lengths):
         if L == 0:
             continue
-        s = scores[r, :L]
-        m = s.max()
-        total = np.exp(s - m).sum()
-        lse[r] = m + math.log(total)
-        p = np.exp(s - lse[r])
-        out[r] = p @ values[:L]
+        rows = np.nonzero(lengths == L)[0]
+        keys = k[:L]
+        s = scale * (q[rows] @ keys.T)             # [rows, L]
+        m = s.max(axis=1)
+        row_lse = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+        lse[rows] = row_lse
+        out[rows] = np.exp(s - row_lse[:, None]) @ keys[:, :D_V]
     return out, lse
 
 

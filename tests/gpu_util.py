@@ -52,17 +52,27 @@ class Score:
     lse_abs: float
     inf_match: bool
     finite: bool
+    # the relative L2 gate applied to each sequence on its own as well, so
+    # that one bad sequence cannot hide in the norm of a large batch
+    worst_seq_rel_l2: float = 0.0
+    worst_seq: int = -1
+    seqs_scored: int = 0
 
     def ok(self) -> bool:
         return (self.finite and self.inf_match and self.max_abs <= OUT_MAX_ABS
-                and self.rel_l2 <= OUT_REL_L2 and self.lse_abs <= LSE_ABS)
+                and self.rel_l2 <= OUT_REL_L2 and self.worst_seq_rel_l2 <= OUT_REL_L2
+                and self.lse_abs <= LSE_ABS)
 
     def __str__(self):
         return (f"max_abs={self.max_abs:.3e} rel_l2={self.rel_l2:.3e} lse_abs={self.lse_abs:.3e} "
+                f"worst_seq_rel_l2={self.worst_seq_rel_l2:.3e} (seq {self.worst_seq} of {self.seqs_scored}) "
                 f"inf_match={self.inf_match} finite={self.finite}")
 
 
 def score(out_bits, lse, ref_out, ref_lse, seqs=None) -> Score:
+    """Gates over the whole output (or the sequences in ``seqs``): element
+    max-abs, relative L2 over all of it and over each sequence, lse abs
+    error over finite entries, and -inf entries in the same places."""
     out = bf16_bits_to_f64(out_bits)
     lse = np.asarray(lse, dtype=np.float64)
     if seqs is not None:
@@ -72,8 +82,17 @@ def score(out_bits, lse, ref_out, ref_lse, seqs=None) -> Score:
     max_abs = float(np.abs(d).max()) if d.size else 0.0
     denom = float(np.linalg.norm(ref_out))
     rel = float(np.linalg.norm(d) / denom) if denom > 0 else float(np.linalg.norm(d))
+    worst, worst_b = 0.0, -1
+    for b in range(out.shape[0]):
+        nb = float(np.linalg.norm(ref_out[b]))
+        eb = float(np.linalg.norm(d[b]))
+        rb = eb / nb if nb > 0 else eb
+        if rb > worst or worst_b < 0:
+            worst, worst_b = rb, b
+    if seqs is not None and worst_b >= 0:
+        worst_b = int(list(seqs)[worst_b])
     ref_inf = np.isneginf(ref_lse)
     inf_match = bool(np.array_equal(ref_inf, np.isneginf(lse)))
     fin = ~ref_inf
     lse_abs = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
-    return Score(max_abs, rel, lse_abs, inf_match, finite)
+    return Score(max_abs, rel, lse_abs, inf_match, finite, worst, worst_b, out.shape[0])

@@ -392,31 +392,97 @@ def pin_fp8_decode_matches_bf16(decode_fp8, ref_bits, seed=35):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2), "FP8 decode differs from BF16 decode"
 
 
-# (r) Quantiser against brute force: for every value, the code whose E4M3
-# value is nearest to |y| = |fl32(x / fl32(amax / 448))| (all 127 magnitudes
-# tried in a plain loop; ties to the even code; above 448 saturating to
-# 0x7E), with y's sign bit. Rows mix tiny values (subnormal codes, negative
-# values that round to zero), exact midpoints and the row maximum.
+# (r) Quantiser against brute force in exact rational arithmetic: for every
+# value, the code whose E4M3 value is nearest to the exact quotient
+# |x| / scale (Fraction arithmetic; all 127 magnitudes tried in a plain loop;
+# ties to the even code; at or above 448 saturating to 0x7E), with x's sign
+# bit, and scale equal to the FP32 number nearest amax / 448. Rows mix tiny
+# values (subnormal codes, negative values that round to zero), values near
+# midpoints and the row maximum.
 def pin_e4m3_quantizer_bruteforce(quantize, decode, seed=36):
+    from fractions import Fraction
     rng = np.random.default_rng(seed)
     rows = (rng.standard_normal((3, 512)) * np.array([1.0, 1e-3, 50.0])[:, None]).astype(np.float32)
     rows[0, :8] = [448.0, -1e-9, 1e-9, 2.0 ** -10, -(2.0 ** -10), 7.5 * 2 ** -9, 0.0, -0.0]
     codes, scale = quantize(rows)
-    mags = [float(decode(np.array([c], dtype=np.uint8))[0]) for c in range(0x7F)]
+    mags = [Fraction(float(decode(np.array([c], dtype=np.uint8))[0])) for c in range(0x7F)]
     for r in range(rows.shape[0]):
-        s32 = np.float32(np.abs(rows[r]).max()) / np.float32(448.0)
-        assert scale[r] == s32, "scale must be fl32(amax / 448)"
-        for d in range(0, 512, 7):
-            y = float(np.float32(rows[r, d]) / s32)
-            a = abs(y)
-            best = 0x7E if a >= 448.0 else None
-            if best is None:
-                dist = [abs(m - a) for m in mags]
+        amax = Fraction(float(np.abs(rows[r]).max()))
+        s_exact = amax / 448
+        # the scale is the FP32 number nearest amax / 448: no FP32 number lies
+        # closer (its two FP32 neighbours are no nearer)
+        s32 = float(scale[r])
+        up, down = np.nextafter(np.float32(s32), np.float32(np.inf)), np.nextafter(np.float32(s32), np.float32(0))
+        assert abs(Fraction(s32) - s_exact) <= abs(Fraction(float(up)) - s_exact), "scale not nearest"
+        assert abs(Fraction(s32) - s_exact) <= abs(Fraction(float(down)) - s_exact), "scale not nearest"
+        for d in range(0, 512, 3):
+            t = abs(Fraction(float(rows[r, d]))) / Fraction(s32)
+            if t >= 448:
+                best = 0x7E
+            else:
+                dist = [abs(m - t) for m in mags]
                 dmin = min(dist)
                 cands = [c for c in range(0x7F) if dist[c] == dmin]
                 best = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
-            want = best | (0x80 if math.copysign(1.0, y) < 0 else 0)
-            assert codes[r, d] == want, f"row {r} col {d}: y={y!r} code 0x{codes[r, d]:02x} want 0x{want:02x}"
+            want = best | (0x80 if math.copysign(1.0, float(rows[r, d])) < 0 else 0)
+            assert codes[r, d] == want, f"row {r} col {d}: t={float(t)!r} code 0x{codes[r, d]:02x} want 0x{want:02x}"
+
+
+# (v) The quotient is exact, not an FP32 quotient. With amax = 11 the scale
+# is fl32(11/448), and for x = 1.03125 (and its multiples by powers of two)
+# the FP32 quotient fl32(x / scale) is exactly 42, the midpoint between the
+# grid values 40 (code 0x62, even) and 44 (code 0x63). The exact quotient
+# lies just above 42, so the nearest value is 44: an FP32 quotient followed
+# by ties-to-even would give 40 instead. A second row checks the mirror case
+# (an exact quotient just below an FP32 midpoint whose even neighbour is
+# above) found by a plain search over BF16 values, and a third a value whose
+# exact quotient is itself a midpoint (ties to even).
+def pin_e4m3_exact_quotient(quantize, decode):
+    from fractions import Fraction
+    row = np.zeros((1, 512), dtype=np.float32)
+    row[0, 0] = 11.0
+    xs = [1.03125 * 2.0 ** k for k in range(-4, 4)]
+    row[0, 1:1 + len(xs)] = xs
+    codes, scale = quantize(row)
+    s32 = np.float32(11.0) / np.float32(448.0)
+    assert scale[0] == s32
+    grid = [float(decode(np.array([c], dtype=np.uint8))[0]) for c in range(0x7F)]
+    mids = {(grid[k] + grid[k + 1]) / 2: k for k in range(0x7E)}
+    for j, x in enumerate(xs, start=1):
+        y32 = float(np.float32(np.float32(x) / s32))
+        assert y32 in mids and mids[y32] % 2 == 0, f"x={x}: FP32 quotient {y32} is not an even-below midpoint"
+        assert Fraction(x) / Fraction(float(s32)) > Fraction(y32), "exact quotient above the FP32 one"
+        val = float(decode(codes[0, j:j + 1])[0])
+        assert val == grid[mids[y32] + 1], f"x={x}: code 0x{codes[0, j]:02x} ({val}), nearest is {grid[mids[y32] + 1]}"
+    assert codes[0, 5] == 0x63 and float(decode(codes[0, 5:6])[0]) == 44.0
+    # mirror case: search BF16 values x <= amax whose FP32 quotient is a
+    # midpoint k with k odd (its even neighbour is the upper one) while the
+    # exact quotient lies below: the nearest value is then the lower, odd code
+    found = None
+    xs_all = (np.arange(0x0080, 0x4200, dtype=np.uint32) << 16).view(np.float32)   # BF16 2^-126 .. 2^5
+    mid_vals = np.array(sorted(mids), dtype=np.float64)
+    for amax in (3.0, 5.0, 6.5, 9.0, 11.0, 13.0):
+        s = np.float32(amax) / np.float32(448.0)
+        xs_a = xs_all[xs_all <= amax]
+        y32s = (xs_a / s).astype(np.float32)
+        for x, y32 in zip(xs_a[np.isin(y32s.astype(np.float64), mid_vals)], y32s[np.isin(y32s.astype(np.float64), mid_vals)]):
+            k = mids[float(y32)]
+            if k % 2 == 1 and Fraction(float(x)) / Fraction(float(s)) < Fraction(float(y32)):
+                found = (amax, float(x), k)
+                break
+        if found:
+            break
+    assert found is not None, "no mirror case in the searched range"
+    amax, x, k = found
+    row2 = np.zeros((1, 512), dtype=np.float32)
+    row2[0, 0], row2[0, 1] = amax, x
+    c2, _ = quantize(row2)
+    assert c2[0, 1] == k, f"amax={amax} x={x}: code 0x{c2[0, 1]:02x}, nearest is 0x{k:02x}"
+    # an exact midpoint: amax = 448 gives scale 1, and 42 = (40 + 44) / 2
+    row3 = np.zeros((1, 512), dtype=np.float32)
+    row3[0, 0], row3[0, 1], row3[0, 2] = 448.0, 42.0, -46.0
+    c3, s3 = quantize(row3)
+    assert float(s3[0]) == 1.0 and c3[0, 1] == 0x62 and c3[0, 2] == 0xE4, "exact midpoints go to the even code"
 
 
 # (s) FP8 append from the physical side, as (k): every page row the placement

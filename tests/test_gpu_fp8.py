@@ -122,8 +122,7 @@ def test_fp8_reference_restart_on_dominant_key():
 def test_fp8_workload_full_size(name):
     inp = make_workload_inputs(name)
     codes, rope, scales = make_fp8_cache(inp, seed=450)
-    seqs = list(range(min(inp.batch, 4)))
-    _check(inp, codes, rope, scales, name, seqs=seqs)
+    _check(inp, codes, rope, scales, name, seqs=list(range(inp.batch)))
 
 
 def test_fp8_rejects_large_query_blocks():
@@ -179,6 +178,50 @@ def test_fp8_append_holes_and_extremes():
         nb[0, 1, 7] = 0x7F00
         nb[0, 2, :512] = 0x8000
         _append_fp8_case(type(inp)(inp.seqlens, inp.block_table, inp.kv_bits, nb), f"holes[{k}]")
+
+
+def _midpoint_rows(n_rows):
+    """BF16 rows whose values put the FP32 quotient fl32(x / scale) exactly on
+    an E4M3 midpoint (so that only the exact quotient decides the code): for
+    several row maxima, every positive BF16 value x <= amax with that
+    property, both signs, after the row maximum itself."""
+    from workloads import bf16_round_bits
+    grid = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    mids = (grid[:-1] + grid[1:]) / 2
+    xs_all = (np.arange(0x0080, 0x7F00, dtype=np.uint32) << 16).view(np.float32)
+    rows = []
+    for amax in (11.0, 3.0, 5.0, 6.5, 9.0, 13.0, 0.75, 1.5, 1e-20, 3e20):
+        amax = float((bf16_round_bits(np.array([amax], dtype=np.float32)).astype(np.uint32) << 16)
+                     .view(np.float32)[0])
+        s = np.float32(amax) / np.float32(448.0)
+        xs = xs_all[xs_all <= amax]
+        hit = xs[np.isin((xs / s).astype(np.float32).astype(np.float64), mids)]
+        vals = np.concatenate([hit, -hit])
+        for k in range(0, max(len(vals), 1), 511):
+            row = np.zeros(576, dtype=np.float32)
+            row[0] = amax
+            chunk = vals[k:k + 511]
+            row[1:1 + len(chunk)] = chunk
+            rows.append(row)
+    rows = np.array(rows[:n_rows], dtype=np.float32)
+    bits = bf16_round_bits(rows)
+    assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), rows), "rows not exact in BF16"
+    return bits
+
+
+def test_fp8_append_exact_quotient_at_midpoints():
+    """Values whose FP32 quotient x / scale lands exactly on an E4M3 midpoint
+    (for amax = 11, x = 1.03125 gives 42, between 40 and 44, while the
+    exact quotient is just above 42): the codes must be those of the exact
+    quotient, bit for bit with the oracle."""
+    from workloads import AppendInputs, make_append_inputs
+    base = make_append_inputs([64, 130, 200, 17], 8, seed=495)
+    rows = _midpoint_rows(base.new_bits.shape[0] * base.new_bits.shape[1])
+    nb = base.new_bits.copy().reshape(-1, 576)
+    nb[:rows.shape[0]] = rows
+    log(f"[case] fp8 append midpoint rows: {rows.shape[0]} rows")
+    _append_fp8_case(AppendInputs(base.seqlens, base.block_table, base.kv_bits, nb.reshape(base.new_bits.shape)),
+                     "midpoints")
 
 
 def test_fp8_append_workload_and_decode():

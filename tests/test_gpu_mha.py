@@ -74,7 +74,7 @@ def test_mha_poisoned_tails_are_ignored():
 
 def test_mha_workload_full_size():
     inp = make_mha_workload("mha_memory_bound")
-    _check(inp, "mha_memory_bound", seqs=[0, 1, 2])
+    _check(inp, "mha_memory_bound")
 
 
 def test_mha_rejects_groups_over_16_rows():

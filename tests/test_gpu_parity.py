@@ -1,8 +1,10 @@
 """HIP path vs the FP64 oracle, element by element, through the C ABI.
 
 Small cases span several pages, ragged tails, empty sequences, the causal
-mask and forced splits; the named workloads run at full size and are
-compared on sampled sequences the oracle computes one by one.
+mask and forced splits; the named workloads run at full size, in the launch
+configuration the benchmark times, and every sequence of every one is
+compared with the oracle (the oracle converts only the pages a sequence
+uses, one sequence at a time).
 """
 
 import numpy as np
@@ -141,19 +143,50 @@ def test_run_to_run_bitwise():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-def _sample_seqs(inp, k):
-    order = np.argsort(inp.seqlens)
-    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2])}
-    rng = np.random.default_rng(0)
-    pick.update(int(x) for x in rng.choice(inp.batch, size=min(k, inp.batch), replace=False))
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_named_workload_full_size(name):
     inp = make_workload_inputs(name)
-    seqs = None if name == "tiny" else _sample_seqs(inp, 6)
-    _check(inp, seqs=seqs, tag=f"workload {name}")
+    _check(inp, seqs=list(range(inp.batch)), tag=f"workload {name}")
+
+
+def _perturb_other_sequences(inp, keep, seed):
+    """New query rows for every sequence not in `keep`, and new cache rows in
+    every page that only those sequences use (lengths and the block table
+    unchanged, so the split plan is unchanged too)."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    q = inp.q_bits.copy()
+    kv = inp.kv_bits.copy()
+    kept_pages = set()
+    for b in keep:
+        kept_pages.update(int(x) for x in inp.block_table[b, :(int(inp.seqlens[b]) + 63) // 64])
+    others = [b for b in range(inp.batch) if b not in keep]
+    for b in others:
+        q[b] = rng.integers(0, 1 << 16, size=q[b].shape, dtype=np.uint16) & 0xBFFF   # finite BF16, |x| < 2
+        for pg in inp.block_table[b, :(int(inp.seqlens[b]) + 63) // 64]:
+            if int(pg) not in kept_pages:
+                kv[int(pg)] = (rng.integers(0, 1 << 16, size=kv[int(pg)].shape, dtype=np.uint16) & 0xBFFF)
+    return dataclasses.replace(inp, q_bits=q, kv_bits=kv)
+
+
+@pytest.mark.parametrize("name", ["memory_bound", "long_context", "multi_token"])
+def test_batch_independence_full_size(name):
+    """Pin (h), batch independence: with the lengths fixed (so the same split
+    plan), changing every other sequence's query and cache rows leaves the
+    kept sequences' outputs and lse bitwise unchanged. Kept: the shortest,
+    the longest and the middle sequence by length (with the default plan the
+    longest is split across partitions)."""
+    inp = make_workload_inputs(name)
+    order = np.argsort(inp.seqlens, kind="stable")
+    keep = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
+    log(f"[case] batch independence {name}: keep {keep} of {inp.batch}")
+    base = run_decode(inp)
+    other = run_decode(_perturb_other_sequences(inp, keep, seed=7))
+    for b in keep:
+        assert np.array_equal(base[0][b], other[0][b]), f"sequence {b} output changed"
+        assert np.array_equal(base[1][b], other[1][b]), f"sequence {b} lse changed"
+    changed = [b for b in range(inp.batch) if b not in keep and not np.array_equal(base[0][b], other[0][b])]
+    assert len(changed) == inp.batch - len(keep), "the perturbation did not reach every other sequence"
 
 
 @pytest.mark.parametrize("h_q,s_q,causal", [(16, 1, False), (128, 2, True)])

@@ -293,6 +293,24 @@ def _quantize_variant(ties_away=False, limit=448.0):
     return quantize
 
 
+def _quantize_fp32_quotient(rows):
+    """The quantiser with the quotient rounded to FP32 first: y = fl32(x /
+    scale), then the E4M3 value nearest y, ties to even. It differs from the
+    exact definition only where fl32(x / scale) lands on a midpoint that the
+    exact quotient misses."""
+    x = np.asarray(rows, dtype=np.float32)
+    amax = np.abs(x).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = (x / scale[:, None]).astype(np.float32)
+    grid = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    mag = np.abs(y).astype(np.float64)
+    idx = np.clip(np.searchsorted(grid, mag), 1, grid.size - 1)
+    lo, hi = grid[idx - 1], grid[idx]
+    pick_hi = ((hi - mag) < (mag - lo)) | (((hi - mag) == (mag - lo)) & (idx % 2 == 0))
+    code = np.where(mag >= 448.0, 0x7E, np.where(pick_hi, idx, idx - 1))
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8), scale
+
+
 def _decode_fp8_variant(rope_scaled=False, scale_ignored=False):
     def decode(q_bits, codes, rope_bits, scales, table, seqlens, scale, causal, seqs=None):
         q = (np.asarray(q_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
@@ -312,6 +330,8 @@ def _run_fp8_pins(decode=None, quantize=None, fp8_decode=None):
     failed = []
     pins = [("table", lambda: P.pin_e4m3_table(decode)),
             ("quantizer", lambda: P.pin_e4m3_quantizer(quantize, decode)),
+            ("quantizer_bruteforce", lambda: P.pin_e4m3_quantizer_bruteforce(quantize, decode)),
+            ("exact_quotient", lambda: P.pin_e4m3_exact_quotient(quantize, decode)),
             ("fp8_vs_bf16", lambda: P.pin_fp8_decode_matches_bf16(fp8_decode, R.mla_decode_ref))]
     with np.errstate(all="ignore"):
         for name, fn in pins:
@@ -328,6 +348,7 @@ FP8_MUTATIONS = {
     "sign_ignored": dict(decode=_e4m3_variant(ignore_sign=True)),
     "quantize_ties_away": dict(quantize=_quantize_variant(ties_away=True)),
     "quantize_limit_240": dict(quantize=_quantize_variant(limit=240.0)),
+    "quantize_fp32_quotient": dict(quantize=_quantize_fp32_quotient),
     "rope_scaled": dict(fp8_decode=_decode_fp8_variant(rope_scaled=True)),
     "scale_ignored": dict(fp8_decode=_decode_fp8_variant(scale_ignored=True)),
 }

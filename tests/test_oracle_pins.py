@@ -72,6 +72,10 @@ def test_e4m3_quantizer_bruteforce():
     P.pin_e4m3_quantizer_bruteforce(oracle.quantize_e4m3_rows, oracle.e4m3_decode)
 
 
+def test_e4m3_exact_quotient():
+    P.pin_e4m3_exact_quotient(oracle.quantize_e4m3_rows, oracle.e4m3_decode)
+
+
 def test_append_fp8_physical_view():
     P.pin_append_fp8_physical_view(oracle.kv_append_fp8_ref, oracle.quantize_e4m3_rows)
 
