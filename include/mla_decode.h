@@ -127,6 +127,23 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
                                        size_t metadata_bytes);
 
 /*
+ * mla_check_metadata_host - whether a host copy of a plan (`metadata`,
+ * `metadata_bytes` bytes, from mla_get_split_metadata_host or copied back
+ * from the device) was built for these arguments: its header (magic, batch,
+ * partition count, per-segment cost, row blocks) against the plan that
+ * mla_decode_fwd (fp8 = 0) or mla_decode_fwd_fp8 (fp8 = 1) builds for
+ * batch, h_q, s_q and num_partitions. The decode kernels run the same test
+ * on the device copy before they read anything else of it.
+ * Returns MLA_OK on a match; MLA_ERR_INVALID_ARG on a mismatch, a NULL or
+ * misaligned buffer, or fp8 not 0/1; MLA_ERR_WORKSPACE_TOO_SMALL when the
+ * buffer is shorter than the header; MLA_ERR_UNSUPPORTED for a shape with no
+ * plan. Uses no GPU (with num_partitions <= 0 the default partition count
+ * comes from the current device's CU count, 256 when there is none).
+ */
+mla_status mla_check_metadata_host(const int32_t* metadata, size_t metadata_bytes, int batch, int h_q,
+                                   int s_q, int num_partitions, int fp8);
+
+/*
  * mla_decode_fwd - MLA decode attention for one layer (see top of file).
  *
  *   q              device bf16 [batch][s_q][h_q][576], contiguous, 16-byte aligned
@@ -140,12 +157,22 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
  *   causal         0 or 1 (bottom-right mask over the s_q new tokens)
  *   metadata       device buffer from mla_get_split_metadata for the same
  *                  seqlens/batch/h_q/s_q/num_partitions, or NULL to have this
- *                  call compute it inside `workspace` first. The plan itself
- *                  is only read; its partial counters (one int per sequence
- *                  and row block, zero as the metadata call writes them) are
- *                  counted up during the call and left at zero again, so one
+ *                  call compute it inside `workspace` first. The kernels
+ *                  check the plan's header against the call's arguments
+ *                  before using it (mla_check_metadata_host); a plan built
+ *                  for other arguments makes the call write NaN into every
+ *                  lse entry and store nothing else (the call itself still
+ *                  returns MLA_OK: the check runs on the device). The plan is
+ *                  only read, except for its partial counters (one int per
+ *                  sequence and row block, zero as the metadata call writes
+ *                  them): when the decode kernel merges split sequences
+ *                  itself it counts the partials there and leaves every
+ *                  counter at zero again when the call completes. So one
  *                  metadata buffer serves any number of calls in stream
- *                  order, but not two calls at the same time
+ *                  order, but not two calls that overlap in time (on one
+ *                  stream or several); a call that does not complete (its
+ *                  context lost) leaves the plan unusable until
+ *                  mla_get_split_metadata rewrites it
  *   num_partitions the value given to mla_get_split_metadata (<= 0: default)
  *   workspace      device scratch, 16-byte aligned, of at least
  *                  mla_workspace_bytes(batch, h_q, s_q, num_partitions) bytes;
@@ -165,6 +192,23 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
                           int h_q, int num_pages, float softmax_scale, int causal,
                           int32_t* metadata, int num_partitions, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * mla_set_plan_override - testing and benchmarking hook (not part of the
+ * attention semantics): forces the decode organisation of every plan built
+ * after the call, process-wide, for BF16 caches.
+ *
+ *   kernel  -1 the default choice (16-row blocks below 64 rows, 64-row
+ *           blocks from 64 rows), 0 always 16-row blocks, 1 always 64-row
+ *   merge   -1 the default choice, 0 split sequences are merged by a combine
+ *           kernel after decode, 1 by the last decode workgroup of each
+ *
+ * The plan (metadata, size queries) and the decode call it serves must be
+ * made under the same setting: a plan built under another kernel choice no
+ * longer matches the call (see mla_check_metadata_host). Returns
+ * MLA_ERR_INVALID_ARG for values outside -1..1.
+ */
+mla_status mla_set_plan_override(int kernel, int merge);
 
 /*
  * Kernel timing for benchmarks (not part of the attention semantics).

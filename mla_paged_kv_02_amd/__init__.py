@@ -349,6 +349,27 @@ def mha_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     return out, lse
 
 
+def set_plan_override(kernel: Optional[str] = None, merge: Optional[str] = None) -> None:
+    """Testing hook (mla_set_plan_override): kernel None | "rows16" | "ws",
+    merge None | "kernel" | "fused"; None restores the default choice. Build
+    plans after setting it."""
+    k = {None: -1, "rows16": 0, "ws": 1}[kernel]
+    m = {None: -1, "kernel": 0, "fused": 1}[merge]
+    check(lib().mla_set_plan_override(k, m), "mla_set_plan_override")
+
+
+def check_metadata_host(metadata: np.ndarray, batch: int, h_q: int, s_q: int, num_partitions: int,
+                        fp8: bool = False) -> bool:
+    """Whether a host copy of a plan matches these call arguments
+    (mla_check_metadata_host)."""
+    meta = np.ascontiguousarray(metadata, dtype=np.int32)
+    st = lib().mla_check_metadata_host(meta.ctypes.data, meta.nbytes, batch, h_q, s_q, num_partitions, int(fp8))
+    if st == 1:
+        return False
+    check(st, "mla_check_metadata_host")
+    return True
+
+
 def timing_enable(enable: bool = True) -> None:
     """Record HIP events around the decode and combine kernels of every
     following decode_fwd call (mla_timing_enable)."""

@@ -14,7 +14,10 @@ import os
 
 import torch  # noqa: F401  (must be loaded before the HIP library)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_decode.so")
+# MLA_DECODE_LIB names another build of the same library (the host-sanitized
+# one the sanitizer tests load); by default the library beside this file.
+LIB_PATH = os.environ.get("MLA_DECODE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libmla_decode.so")
 
 _c_int = ctypes.c_int
 _c_size = ctypes.c_size_t
@@ -31,6 +34,7 @@ SIGNATURES = {
     "mla_get_split_metadata": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "mla_get_split_metadata_fp8": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "mla_get_split_metadata_host": (_c_int, [_c_ptr, _c_int, _c_int, _c_int, _c_int, _c_ptr, _c_size]),
+    "mla_check_metadata_host": (_c_int, [_c_ptr, _c_size, _c_int, _c_int, _c_int, _c_int, _c_int]),
     "mla_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                 _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_kv_append": (_c_int, [_c_ptr, _c_int, _c_int, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr]),
@@ -42,6 +46,7 @@ SIGNATURES = {
                                     _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr, _c_ptr, _c_ptr]),
     "mla_mha_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_float, _c_int, _c_ptr, _c_ptr, _c_ptr]),
+    "mla_set_plan_override": (_c_int, [_c_int, _c_int]),
     "mla_timing_enable": (_c_int, [_c_int]),
     "mla_timing_collect": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(_c_int)]),

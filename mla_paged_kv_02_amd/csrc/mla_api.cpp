@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -45,17 +46,10 @@ int current_cu_count() {
     return g_cu_count[dev];
 }
 
-// Optional override of the kernel choice, read once: -1 when unset.
-int kernel_override() {
-    static int v = []() {
-        const char* e = std::getenv("MLA_DECODE_KERNEL");
-        if (!e) return -1;
-        if (!std::strcmp(e, "rows16")) return static_cast<int>(DecodeKernel::Rows16);
-        if (!std::strcmp(e, "ws")) return static_cast<int>(DecodeKernel::WaveSplit);
-        return -1;
-    }();
-    return v;
-}
+// Process-wide overrides of the kernel choice and of where split sequences
+// are merged (mla_set_plan_override); -1 keeps the plan's own choice.
+std::atomic<int> g_kernel_override{-1};
+std::atomic<int> g_merge_override{-1};
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -108,7 +102,7 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.h_q = h_q;
     pl.s_q = s_q;
     pl.M = (int)m;
-    // Kernel choice (MLA_DECODE_KERNEL=rows16|ws overrides it): 16-row blocks
+    // Kernel choice (mla_set_plan_override can force one): 16-row blocks
     // below 64 rows, 64-row blocks from 64 rows on (at exactly 64 the 16-row
     // kernel would stream every page four times, once per row block, and
     // its per-CU load rate then bounds it: on the long-context workload the
@@ -116,8 +110,9 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // cache has only the 16-row kernel: its plans take it up to 64 rows.
     if (fp8 && pl.M > 64) return false;
     DecodeKernel k = (pl.M < 64 || fp8) ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
-    const int ov = kernel_override();
-    if (ov >= 0) k = static_cast<DecodeKernel>(ov);
+    const int ov = g_kernel_override.load(std::memory_order_relaxed);
+    if (ov == 0 && !fp8) k = DecodeKernel::Rows16;
+    if (ov == 1 && !fp8) k = DecodeKernel::WaveSplit;
     const int tm = k == DecodeKernel::Rows16 ? 16 : 64;
     pl.kernel = k;
     pl.tm = tm;
@@ -147,12 +142,10 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // are large enough that writing them through to the coherent level costs
     // more than a second kernel (128 heads, 128 sequences of 4096 tokens:
     // call 186-190 vs 192-195 us); a combine kernel merges them instead
-    // (MLA_COMBINE=kernel|fused, read at every call, overrides the choice).
+    // (mla_set_plan_override can force either).
     pl.fused_combine = pl.P <= pl.batch && pl.M < 128;
-    if (const char* e = std::getenv("MLA_COMBINE")) {
-        if (!std::strcmp(e, "kernel")) pl.fused_combine = false;
-        if (!std::strcmp(e, "fused")) pl.fused_combine = true;
-    }
+    const int mo = g_merge_override.load(std::memory_order_relaxed);
+    if (mo >= 0) pl.fused_combine = mo == 1;
     *plan = pl;
     return true;
 }
@@ -255,6 +248,20 @@ mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q
     return get_split_metadata(seqlens, batch, h_q, s_q, num_partitions, metadata, metadata_bytes_, stream, true);
 }
 
+mla_status mla_check_metadata_host(const int32_t* metadata, size_t metadata_bytes_, int batch, int h_q,
+                                   int s_q, int num_partitions, int fp8) {
+    if (!metadata || !aligned(metadata, 4) || (fp8 != 0 && fp8 != 1)) return MLA_ERR_INVALID_ARG;
+    if (batch < 1 || h_q < 1 || s_q < 1 || num_partitions > 65536) return MLA_ERR_INVALID_ARG;
+    if (metadata_bytes_ < (size_t)kMetaHeader * 4) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    Plan pl;
+    if (!make_plan(batch, h_q, s_q, num_partitions, num_partitions > 0 ? 0 : current_cu_count(), &pl, fp8 != 0))
+        return MLA_ERR_UNSUPPORTED;
+    return plan_header_matches(metadata[0], metadata[1], metadata[2], metadata[3], metadata[8], pl.batch, pl.P,
+                               pl.cseg, pl.R)
+               ? MLA_OK
+               : MLA_ERR_INVALID_ARG;
+}
+
 mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_q, int s_q,
                                        int num_partitions, int32_t* metadata,
                                        size_t metadata_bytes_) {
@@ -339,6 +346,7 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
     a.M = pl.M;
     a.R = pl.R;
     a.P = pl.P;
+    a.cseg = pl.cseg;
     a.scale_log2 = softmax_scale * kLog2e;
     a.causal = causal;
     CallEvents* te = timing_slot();
@@ -372,6 +380,13 @@ mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t
     return decode_fwd_impl(q, kv_cache, block_table, max_blocks_per_seq, seqlens, batch, s_q, h_q, num_pages,
                            softmax_scale, causal, metadata, num_partitions, workspace, workspace_bytes_, out,
                            lse, stream, true);
+}
+
+mla_status mla_set_plan_override(int kernel, int merge) {
+    if (kernel < -1 || kernel > 1 || merge < -1 || merge > 1) return MLA_ERR_INVALID_ARG;
+    g_kernel_override.store(kernel, std::memory_order_relaxed);
+    g_merge_override.store(merge, std::memory_order_relaxed);
+    return MLA_OK;
 }
 
 mla_status mla_timing_enable(int enable) {

@@ -16,6 +16,7 @@
 // 16 waves of a block share one item's partials and sum them through LDS, so
 // that each wave has only a round trip or two of loads to wait for.
 #include "mla_common.h"
+#include "mla_fused_combine.h"
 #include "mla_internal.h"
 #include "mla_sched.h"
 
@@ -35,6 +36,11 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
     constexpr int kWaves = kWPI > 4 ? kWPI : 4;
     constexpr int kItems = kWaves / kWPI;
     __shared__ f32x4 red[kWPI > 1 ? kWaves : 1][64];
+    // a plan built for other arguments: the decode kernel has written NaN
+    // into every lse entry and nothing else; neither does this kernel
+    if (!plan_header_matches(ld_plan_word(a.meta, 0), ld_plan_word(a.meta, 1), ld_plan_word(a.meta, 2),
+                             ld_plan_word(a.meta, 3), ld_plan_word(a.meta, 8), a.batch, a.P, a.cseg, a.R))
+        return;
     // one-dimensional grid, the blocks of a sequence consecutive
     const int per_b = __builtin_amdgcn_readfirstlane((2 * a.M + kItems - 1) / kItems);
     const int b = blockIdx.x / per_b;

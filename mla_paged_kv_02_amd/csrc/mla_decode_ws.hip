@@ -110,6 +110,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     const int g = lane >> 4;
     const int i16 = lane & 15;
 
+    if (!plan_matches_or_poison<512>(a)) return;
     const int bid = blockIdx.x;
     const int rb = (bid >> 3) % a.R;
     const int p = ((bid >> 3) / a.R) * 8 + (bid & 7);

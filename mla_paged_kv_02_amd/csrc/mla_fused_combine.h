@@ -20,6 +20,26 @@
 
 namespace mla {
 
+__device__ __forceinline__ int32_t ld_plan_word(const int32_t* p, int i) {
+    return reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(reinterpret_cast<uintptr_t>(p))[i];
+}
+
+// The plan check every decode kernel runs before it reads anything else of
+// the plan: true if the header matches the call. Otherwise the workgroups
+// write NaN into every lse entry between them (the visible sign of a plan
+// built for other arguments) and the kernel stores nothing else.
+template <int kThreads>
+__device__ __forceinline__ bool plan_matches_or_poison(const DecodeArgs& a) {
+    const bool ok = plan_header_matches(ld_plan_word(a.meta, 0), ld_plan_word(a.meta, 1), ld_plan_word(a.meta, 2),
+                                        ld_plan_word(a.meta, 3), ld_plan_word(a.meta, 8), a.batch, a.P, a.cseg,
+                                        a.R);
+    if (ok) return true;
+    const size_t n = (size_t)a.batch * a.M;
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+        a.lse[i] = __builtin_nanf("");
+    return false;
+}
+
 // Merges the partials of rows row0 .. row0 + nrows - 1 (< M) of sequence b,
 // slots base .. base + cnt - 1, into out and lse. All kThreads threads of
 // the workgroup call it; each owns one row and 512 / (kThreads / nrows)

@@ -55,6 +55,7 @@ struct DecodeArgs {
     int max_blocks;
     int batch, s_q, h_q, M;
     int R, P;
+    int cseg;          // the plan's per-segment cost (checked against its header)
     int lse_stride;    // split-partial slots of the plan
     float scale_log2;  // softmax_scale * log2(e)
     int causal;

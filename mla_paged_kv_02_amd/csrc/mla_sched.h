@@ -56,6 +56,16 @@ MLA_HD int meta_counters(int batch, int num_partitions) {
     return kMetaHeader + kPartInts * num_partitions + 4 * batch;
 }
 
+// Whether a plan's header ([0] magic, [1] batch, [2] P, [3] cseg, [8] R)
+// is the one a decode call with these arguments would build. The decode and
+// combine kernels test it before reading anything else of the plan, and the
+// host check of a host copy uses the same test.
+MLA_HD bool plan_header_matches(int32_t magic, int32_t batch_m, int32_t p_m, int32_t cseg_m, int32_t r_m,
+                                int batch, int num_partitions, int cseg, int row_blocks) {
+    return magic == kMetaMagic && batch_m == batch && p_m == num_partitions && cseg_m == cseg &&
+           r_m == row_blocks;
+}
+
 MLA_HD int32_t pages_of(int32_t seqlen) { return (seqlen + kPageSize - 1) / kPageSize; }
 
 // Length of sequence b on the cost line.

@@ -8,6 +8,38 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def pytest_addoption(parser):
+    parser.addoption("--decode-kernel", default=None, choices=("rows16", "ws"),
+                     help="GPU tests: force every BF16 decode plan onto one kernel organisation "
+                          "(mla_set_plan_override)")
+
+
+@pytest.fixture(autouse=True)
+def _plan_override(request):
+    """Applies --decode-kernel to GPU tests, and restores the default plan
+    choice after any test that changed it."""
+    kernel = request.config.getoption("--decode-kernel")
+    touched = kernel is not None or "plan_override" in request.fixturenames
+    if touched:
+        import mla_paged_kv_02_amd as mla
+        mla.set_plan_override(kernel=kernel)
+    yield
+    if touched:
+        import mla_paged_kv_02_amd as mla
+        mla.set_plan_override()
+
+
+@pytest.fixture
+def plan_override(request):
+    """Setter for mla_set_plan_override inside a test (kept with --decode-kernel)."""
+    import mla_paged_kv_02_amd as mla
+    kernel = request.config.getoption("--decode-kernel")
+
+    def set_(merge=None):
+        mla.set_plan_override(kernel=kernel, merge=merge)
+    return set_
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 

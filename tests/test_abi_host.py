@@ -249,3 +249,63 @@ def _mha(**kw):
 ])
 def test_mha_argument_checks(kw, status):
     assert _mha(**kw) == status
+
+
+def _host_plan(seqlens, h_q, s_q, parts):
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    lib = _lib.lib()
+    nbytes = lib.mla_metadata_bytes(len(sl), h_q, s_q, parts)
+    meta = np.zeros(nbytes // 4, dtype=np.int32)
+    assert lib.mla_get_split_metadata_host(sl.ctypes.data, len(sl), h_q, s_q, parts, meta.ctypes.data,
+                                           meta.nbytes) == OK
+    return meta
+
+
+def _check_meta(meta, batch, h_q, s_q, parts, fp8=0, nbytes=None):
+    return _lib.lib().mla_check_metadata_host(meta.ctypes.data, meta.nbytes if nbytes is None else nbytes,
+                                              batch, h_q, s_q, parts, fp8)
+
+
+def test_plan_header_check_on_host_plans():
+    """The header test the decode kernels run before using a plan, through
+    the host copy of the plan builder's output: a plan matches the call it
+    was built for and no call that would read it at other offsets."""
+    lens = [300, 70, 129, 5000]
+    for h_q, s_q, parts in [(16, 1, 64), (64, 1, 64), (128, 2, 32), (16, 3, 8)]:
+        meta = _host_plan(lens, h_q, s_q, parts)
+        assert _check_meta(meta, 4, h_q, s_q, parts) == OK
+        assert _check_meta(meta, 4, h_q, s_q, parts * 2) == INVALID      # another partition count
+        assert _check_meta(meta, 3, h_q, s_q, parts) == INVALID          # another batch
+        assert _check_meta(meta, 4, h_q * 2, s_q, parts) == INVALID      # other row blocks
+        bad = meta.copy()
+        bad[0] ^= 1
+        assert _check_meta(bad, 4, h_q, s_q, parts) == INVALID           # not a plan
+        assert _check_meta(meta, 4, h_q, s_q, parts, nbytes=60) == TOO_SMALL
+    # 64 rows: the BF16 call uses 64-row blocks (R = 1), the FP8 call 16-row
+    # blocks (R = 4); 16 rows: both use 16-row blocks and share the plan
+    assert _check_meta(_host_plan(lens, 64, 1, 64), 4, 64, 1, 64, fp8=1) == INVALID
+    assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 16, 1, 64, fp8=1) == OK
+    assert _lib.lib().mla_check_metadata_host(None, 1024, 4, 16, 1, 64, 0) == INVALID
+    assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 16, 1, 64, fp8=2) == INVALID
+    assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 512, 4, 64) == UNSUPPORTED
+
+
+def test_plan_override_is_checked_and_shapes_the_plan():
+    lib = _lib.lib()
+    assert lib.mla_set_plan_override(2, -1) == INVALID
+    assert lib.mla_set_plan_override(-1, -2) == INVALID
+    lens = [300, 70, 129, 5000]
+    try:
+        assert lib.mla_set_plan_override(1, -1) == OK          # 64-row blocks at 16 rows: R = 1
+        ws_plan = _host_plan(lens, 32, 1, 64)
+        assert ws_plan[8] == 1
+        assert lib.mla_set_plan_override(0, -1) == OK          # 16-row blocks at 64 rows: R = 4
+        r16_plan = _host_plan(lens, 64, 1, 64)
+        assert r16_plan[8] == 4
+        # a plan built under one setting does not match a call under the default
+        assert lib.mla_set_plan_override(-1, -1) == OK
+        assert _check_meta(ws_plan, 4, 32, 1, 64) == INVALID
+        assert _check_meta(r16_plan, 4, 64, 1, 64) == INVALID
+    finally:
+        lib.mla_set_plan_override(-1, -1)

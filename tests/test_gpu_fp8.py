@@ -90,8 +90,8 @@ def test_fp8_poisoned_tails_are_ignored():
 
 
 @pytest.mark.parametrize("mode", ["fused", "kernel"])
-def test_fp8_combine_modes(mode, monkeypatch):
-    monkeypatch.setenv("MLA_COMBINE", mode)
+def test_fp8_combine_modes(mode, plan_override):
+    plan_override(merge=mode)
     inp = make_inputs([0, 900, 3, 2049, 64, 1500, 0, 777], 1, 16, seed=330)
     codes, rope, scales = make_fp8_cache(inp, seed=430)
     for parts in (8, 64):

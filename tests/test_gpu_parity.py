@@ -190,7 +190,7 @@ def test_batch_independence_full_size(name):
 
 
 @pytest.mark.parametrize("h_q,s_q,causal", [(16, 1, False), (128, 2, True)])
-def test_fused_combine_counters_and_modes(h_q, s_q, causal, monkeypatch):
+def test_fused_combine_counters_and_modes(h_q, s_q, causal, plan_override):
     """The merge inside the decode kernel (last workgroup of a split
     sequence) against the combine kernel: same results, and the partial
     counters in the metadata are zero again after every call, so repeated
@@ -207,7 +207,7 @@ def test_fused_combine_counters_and_modes(h_q, s_q, causal, monkeypatch):
         host = mla.split_metadata_host(inp.seqlens, h_q, s_q, parts)
         results = {}
         for mode in ("fused", "kernel", "fused"):
-            monkeypatch.setenv("MLA_COMBINE", mode)
+            plan_override(merge=mode)
             out, lse = mla.decode_fwd(q, kv, bt, sl, inp.scale, inp.causal, meta=meta,
                                       num_partitions=parts)
             torch.cuda.synchronize()
@@ -291,3 +291,47 @@ def test_pages_past_4_gib():
     assert np.array_equal(got, ref_kv), "append into pages past 4 GiB"
     del big
     torch.cuda.empty_cache()
+
+
+def test_mismatched_plan_writes_nan_lse_and_nothing_else():
+    """A plan built for other arguments, passed through the C ABI (the Python
+    binding refuses it first): the decode kernel finds the header mismatch
+    before it reads anything else, writes NaN into every lse entry and stores
+    nothing else. Every case keeps the kernel's reads of the plan inside the
+    buffer (the plan has at least as many partition records as the call)."""
+    import ctypes
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from mla_paged_kv_02_amd import _lib
+    from gpu_util import to_device
+    from workloads import make_fp8_cache, pack_fp8_pages
+    inp = make_inputs([300, 70, 129], 1, 64, seed=95)
+    q, kv, bt, sl = to_device(inp)
+    pages = torch.from_numpy(pack_fp8_pages(*make_fp8_cache(inp, seed=96))).cuda()
+    cases = [  # (tag, plan h_q, plan partitions, call h_q, call partitions, fp8 call)
+        ("partition count", 64, 128, 64, 64, False),
+        ("row blocks", 64, 64, 128, 64, False),
+        ("BF16 plan into the FP8 call", 64, 64, 64, 64, True),
+        ("16-row plan, other partition count", 16, 64, 16, 32, False),
+    ]
+    for tag, ph, pp, ch, cp, fp8 in cases:
+        meta = mla.get_split_metadata(sl, ph, 1, pp)
+        host = meta.metadata.cpu().numpy()
+        assert _lib.lib().mla_check_metadata_host(host.ctypes.data, host.nbytes, inp.batch, ch, 1, cp,
+                                                  int(fp8)) == 1, tag
+        qc = q if ch == 64 else torch.cat([q, q], dim=2).contiguous()
+        out = torch.full((inp.batch, 1, ch, 512), 1.5, dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros((inp.batch, 1, ch), dtype=torch.float32, device="cuda")
+        ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+        fn = _lib.lib().mla_decode_fwd_fp8 if fp8 else _lib.lib().mla_decode_fwd
+        cache = pages if fp8 else kv
+        log(f"[case] mismatched plan: {tag}")
+        st = fn(qc.data_ptr(), cache.data_ptr(), bt.data_ptr(), bt.shape[1], sl.data_ptr(), inp.batch, 1, ch,
+                cache.shape[0], ctypes.c_float(inp.scale), 0, meta.metadata.data_ptr(), cp, ws.data_ptr(),
+                ws.numel(), out.data_ptr(), lse.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert st == 0, tag
+        assert torch.isnan(lse).all().item(), f"{tag}: lse not NaN everywhere"
+        assert (out.float() == 1.5).all().item(), f"{tag}: out was written"
+        # the plan itself is untouched
+        assert np.array_equal(meta.metadata.cpu().numpy(), host), f"{tag}: plan changed"
