@@ -66,7 +66,8 @@ typedef enum mla_status {
     MLA_ERR_UNSUPPORTED = 2,          /* shape outside what the kernels cover   */
     MLA_ERR_MISALIGNED = 3,           /* pointer alignment requirement broken   */
     MLA_ERR_WORKSPACE_TOO_SMALL = 4,  /* metadata or workspace buffer too small */
-    MLA_ERR_HIP = 5                   /* a HIP runtime call or launch failed    */
+    MLA_ERR_HIP = 5,                  /* a HIP runtime call or launch failed    */
+    MLA_ERR_SCRATCH_LIMIT = 6         /* beyond mla_decode_fwd_noalloc's scratch */
 } mla_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -192,6 +193,38 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
                           int h_q, int num_pages, float softmax_scale, int causal,
                           int32_t* metadata, int num_partitions, void* workspace,
                           size_t workspace_bytes, void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_fwd_noalloc - mla_decode_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without
+ * `workspace`, the same results, bit for bit. It calls no hipMalloc,
+ * hipFree or other allocating routine; the split partials (and the plan,
+ * when `metadata` is NULL) live in a scratch array of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds in each GPU's memory from
+ * its first call there until the process ends.
+ *
+ * Limit: a call whose workspace need exceeds MLA_NOALLOC_SCRATCH_BYTES
+ * returns MLA_ERR_SCRATCH_LIMIT and enqueues nothing; every call with
+ * mla_workspace_bytes(batch, h_q, s_q, num_partitions) <=
+ * MLA_NOALLOC_SCRATCH_BYTES is accepted (with the default partition count
+ * that covers, for example, 128 sequences at 128 heads and 132 sequences of
+ * two tokens at 128 heads).
+ *
+ * All calls on one GPU share its scratch and leave their contents in it;
+ * nothing there needs to start at zero (a plan computed in the scratch is
+ * written whole by each call). Calls that overlap in time on one GPU (on
+ * different streams, or different host threads) race on the scratch and
+ * give undefined results: order them on one stream. The first call on a
+ * device looks up the scratch's address (not an allocation; it may load
+ * the library's code object on that device).
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (72u << 20)
+
+mla_status mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                  int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q, int h_q,
+                                  int num_pages, float softmax_scale, int causal, int32_t* metadata,
+                                  int num_partitions, void* out, float* lse, void* stream);
 
 /*
  * mla_set_plan_override - testing and benchmarking hook (not part of the

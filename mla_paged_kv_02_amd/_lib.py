@@ -47,6 +47,8 @@ SIGNATURES = {
     "mla_mha_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_float, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "mla_set_plan_override": (_c_int, [_c_int, _c_int]),
+    "mla_decode_fwd_noalloc": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
+                                        _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "mla_timing_enable": (_c_int, [_c_int]),
     "mla_timing_collect": (_c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(_c_int)]),
@@ -55,7 +57,7 @@ SIGNATURES = {
 MLA_OK = 0
 STATUS_NAMES = {
     0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_MISALIGNED",
-    4: "MLA_ERR_WORKSPACE_TOO_SMALL", 5: "MLA_ERR_HIP",
+    4: "MLA_ERR_WORKSPACE_TOO_SMALL", 5: "MLA_ERR_HIP", 6: "MLA_ERR_SCRATCH_LIMIT",
 }
 
 

@@ -178,6 +178,9 @@ const char* mla_status_string(int status) {
         case MLA_ERR_MISALIGNED: return "MLA_ERR_MISALIGNED: pointer alignment";
         case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: buffer too small";
         case MLA_ERR_HIP: return "MLA_ERR_HIP: HIP runtime or launch failure";
+        case MLA_ERR_SCRATCH_LIMIT:
+            return "MLA_ERR_SCRATCH_LIMIT: the call needs more scratch than the allocation-free entry point "
+                   "holds (MLA_NOALLOC_SCRATCH_BYTES); use mla_decode_fwd with a workspace";
         default: return "MLA_ERR_UNKNOWN";
     }
 }
@@ -282,13 +285,45 @@ mla_status mla_get_split_metadata_host(const int32_t* seqlens, int batch, int h_
 
 namespace {
 
-// Both decode entry points: the BF16 cache, or FP8 pages (16-row kernel only).
+// Scratch of the allocation-free decode call (mla_decode_fwd_noalloc): its
+// split partials and, when the caller passes no plan, the plan. One copy per
+// GPU, held from the first such call on that GPU until the process ends; the
+// calls on one GPU share it. In host code `scratch` is only a handle for the
+// symbol lookup below: the device address is what scratch_address returns.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's scratch, looked up once per device
+// with that device current; nullptr if the lookup failed.
+void* scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+// Both decode entry points: the BF16 cache, or FP8 pages (16-row kernel
+// only). `noalloc`: workspace and its size are ignored and the call runs in
+// this device's scratch instead (never timed).
 mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* block_table,
                            int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q,
                            int h_q, int num_pages, float softmax_scale, int causal,
                            int32_t* metadata, int num_partitions, void* workspace,
-                           size_t workspace_bytes_, void* out, float* lse, void* stream, bool fp8) {
-    if (!q || !kv_cache || !block_table || !seqlens || !workspace || !out || !lse)
+                           size_t workspace_bytes_, void* out, float* lse, void* stream, bool fp8,
+                           bool noalloc = false) {
+    if (!q || !kv_cache || !block_table || !seqlens || (!workspace && !noalloc) || !out || !lse)
         return MLA_ERR_INVALID_ARG;
     if (batch < 1 || s_q < 1 || h_q < 1 || max_blocks_per_seq < 1 || num_pages < 1)
         return MLA_ERR_INVALID_ARG;
@@ -300,7 +335,7 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
     if (num_partitions > 65536) return MLA_ERR_INVALID_ARG;
     if ((long long)h_q * s_q > MLA_MAX_ROWS) return MLA_ERR_UNSUPPORTED;
     if ((long long)max_blocks_per_seq * batch > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
-    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(workspace, 16))
+    if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || (!noalloc && !aligned(workspace, 16)))
         return MLA_ERR_MISALIGNED;
     if (!aligned(block_table, 4) || !aligned(seqlens, 4) || !aligned(lse, 4) ||
         (metadata && !aligned(metadata, 4)))
@@ -315,6 +350,12 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
         pl.kernel = DecodeKernel::Rows16Fp8;
     }
     const WorkspaceLayout wl = workspace_layout(pl, metadata == nullptr);
+    if (noalloc) {
+        if (wl.total > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_LIMIT;
+        workspace = scratch_address();
+        if (!workspace) return MLA_ERR_HIP;
+        workspace_bytes_ = MLA_NOALLOC_SCRATCH_BYTES;
+    }
     if (workspace_bytes_ < wl.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -349,7 +390,7 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
     a.cseg = pl.cseg;
     a.scale_log2 = softmax_scale * kLog2e;
     a.causal = causal;
-    CallEvents* te = timing_slot();
+    CallEvents* te = noalloc ? nullptr : timing_slot();
     if (te && hipEventRecord(te->ev[0], st) != hipSuccess) return MLA_ERR_HIP;
     if (launch_decode(pl, a, st) != hipSuccess) return MLA_ERR_HIP;
     if (te && hipEventRecord(te->ev[1], st) != hipSuccess) return MLA_ERR_HIP;
@@ -370,6 +411,15 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
     return decode_fwd_impl(q, kv_cache, block_table, max_blocks_per_seq, seqlens, batch, s_q, h_q, num_pages,
                            softmax_scale, causal, metadata, num_partitions, workspace, workspace_bytes_, out,
                            lse, stream, false);
+}
+
+mla_status mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                  int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q, int h_q,
+                                  int num_pages, float softmax_scale, int causal, int32_t* metadata,
+                                  int num_partitions, void* out, float* lse, void* stream) {
+    return decode_fwd_impl(q, kv_cache, block_table, max_blocks_per_seq, seqlens, batch, s_q, h_q, num_pages,
+                           softmax_scale, causal, metadata, num_partitions, nullptr, 0, out, lse, stream, false,
+                           true);
 }
 
 mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t* block_table,

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.lib()
-    for code in range(6):
+    for code in range(7):
         assert lib.mla_status_string(code).decode().startswith(_lib.STATUS_NAMES[code])
     assert lib.mla_abi_version() >> 16 == 1
 
@@ -309,3 +309,29 @@ def test_plan_override_is_checked_and_shapes_the_plan():
         assert _check_meta(r16_plan, 4, 64, 1, 64) == INVALID
     finally:
         lib.mla_set_plan_override(-1, -1)
+
+
+def _noalloc(**kw):
+    args = dict(q=FAKE, kv=FAKE, bt=FAKE, maxb=4, seqlens=FAKE, batch=2, s_q=1, h_q=16,
+                pages=8, scale=1 / 24, causal=0, meta=FAKE, nparts=64, out=FAKE, lse=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_decode_fwd_noalloc(
+        args["q"], args["kv"], args["bt"], args["maxb"], args["seqlens"], args["batch"],
+        args["s_q"], args["h_q"], args["pages"], ctypes.c_float(args["scale"]), args["causal"],
+        args["meta"], args["nparts"], args["out"], args["lse"], args["stream"])
+
+
+SCRATCH_LIMIT = 6
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kv=None), INVALID), (dict(out=None), INVALID), (dict(lse=None), INVALID),
+    (dict(batch=0), INVALID), (dict(scale=-1.0), INVALID), (dict(scale=0.0), INVALID), (dict(causal=2), INVALID),
+    (dict(h_q=128, s_q=16), UNSUPPORTED), (dict(q=FAKE + 8), MISALIGNED), (dict(meta=FAKE + 2), MISALIGNED),
+    # 4096 partitions of 1024 rows: 32 GiB of partials, far past the scratch
+    (dict(h_q=128, s_q=8, nparts=4096), SCRATCH_LIMIT),
+    (dict(batch=9000, h_q=128, s_q=8, nparts=512, meta=None), SCRATCH_LIMIT),
+])
+def test_noalloc_argument_checks(kw, status):
+    """Checked on the host before any HIP call, the scratch limit included."""
+    assert _noalloc(**kw) == status

@@ -1,0 +1,83 @@
+"""The allocation-free decode call (mla_decode_fwd_noalloc) through the C ABI
+against mla_decode_fwd with a workspace: the same results bit for bit, and
+both within the oracle's gates, on consecutive calls that share the GPU's
+scratch (a large call, then a smaller one, then the large one again)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import log, score, to_device
+from workloads import make_inputs, make_workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _call(inp, noalloc, use_meta, parts=0):
+    import torch
+    import mla_paged_kv_02_amd as mla
+    from mla_paged_kv_02_amd import _lib
+    q, kv, bt, sl = to_device(inp)
+    out = torch.empty((inp.batch, inp.s_q, inp.h_q, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((inp.batch, inp.s_q, inp.h_q), dtype=torch.float32, device="cuda")
+    meta = mla.get_split_metadata(sl, inp.h_q, inp.s_q, parts) if use_meta else None
+    mptr = meta.metadata.data_ptr() if meta is not None else None
+    stream = torch.cuda.current_stream().cuda_stream
+    lib = _lib.lib()
+    if noalloc:
+        st = lib.mla_decode_fwd_noalloc(q.data_ptr(), kv.data_ptr(), bt.data_ptr(), bt.shape[1], sl.data_ptr(),
+                                        inp.batch, inp.s_q, inp.h_q, kv.shape[0], ctypes.c_float(inp.scale),
+                                        int(inp.causal), mptr, parts, out.data_ptr(), lse.data_ptr(), stream)
+    else:
+        nbytes = mla.workspace_bytes(inp.batch, inp.h_q, inp.s_q, parts)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        st = lib.mla_decode_fwd(q.data_ptr(), kv.data_ptr(), bt.data_ptr(), bt.shape[1], sl.data_ptr(),
+                                inp.batch, inp.s_q, inp.h_q, kv.shape[0], ctypes.c_float(inp.scale),
+                                int(inp.causal), mptr, parts, ws.data_ptr(), nbytes, out.data_ptr(),
+                                lse.data_ptr(), stream)
+    assert st == 0, f"status {st}"
+    torch.cuda.synchronize()
+    return out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()
+
+
+def _compare(inp, tag, use_meta, parts=0):
+    log(f"[case] noalloc {tag}: B={inp.batch} s_q={inp.s_q} h_q={inp.h_q} meta={use_meta} parts={parts}")
+    a = _call(inp, False, use_meta, parts)
+    b = _call(inp, True, use_meta, parts)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), f"{tag}: differs from mla_decode_fwd"
+    ref_out, ref_lse = oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens, inp.scale,
+                                             inp.causal, seqs=list(range(inp.batch)))
+    s = score(b[0], b[1], ref_out, ref_lse)
+    log(f"  {s}")
+    assert s.ok(), f"{tag}: {s}"
+
+
+def test_noalloc_matches_workspace_call_on_consecutive_calls():
+    big = make_inputs([3000, 77, 4097, 1500, 0, 9000, 640], 2, 64, seed=61, causal=True)
+    small = make_inputs([37, 100, 1], 1, 16, seed=62)
+    _compare(big, "large, plan computed in the scratch", use_meta=False)
+    _compare(small, "smaller, plan computed in the scratch", use_meta=False)
+    _compare(small, "smaller, caller's plan, merge in the decode kernel", use_meta=True, parts=8)
+    _compare(big, "large again, caller's plan", use_meta=True)
+
+
+def test_noalloc_at_the_largest_workloads():
+    """The 128-head workloads need the most scratch (about 64 MiB), the
+    long-context one the most partials per sequence."""
+    for name in ("multi_token", "long_context", "memory_bound"):
+        _compare(make_workload_inputs(name), name, use_meta=False)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    import torch
+    from mla_paged_kv_02_amd import _lib
+    inp = make_inputs([10, 20], 8, 128, seed=63)                # M = 1024 rows
+    q, kv, bt, sl = to_device(inp)
+    out = torch.empty((2, 8, 128, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((2, 8, 128), dtype=torch.float32, device="cuda")
+    st = _lib.lib().mla_decode_fwd_noalloc(q.data_ptr(), kv.data_ptr(), bt.data_ptr(), bt.shape[1], sl.data_ptr(),
+                                           2, 8, 128, kv.shape[0], ctypes.c_float(inp.scale), 1, None, 4096,
+                                           out.data_ptr(), lse.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 6, f"status {st}, expected MLA_ERR_SCRATCH_LIMIT"
