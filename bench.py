@@ -249,11 +249,30 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     call_ms_mean = float(call_ms.mean())
     dec_ms = dec_ms_sum / steps
     comb_ms = comb_ms_sum / steps
+    # (3) per layer: the attention call alone, back to back over the rotated
+    # caches with one plan (a decode step builds it once for every layer),
+    # between two events, all launches queued behind a device-side spin so
+    # that the host's launch cost stays out
+    meta = mla.get_split_metadata(sl, w.h_q, w.s_q, num_partitions, fp8=fp8)
+    for i in range(2):
+        decode(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hold_queue(0.1 * steps + 0.5)
+    l0.record(stream)
+    for i in range(steps):
+        decode(q, kvs[i % copies], bt, sl, inp.scale, inp.causal, meta=meta, out=out, lse=lse, workspace=ws)
+    l1.record(stream)
+    torch.cuda.synchronize()
+    layer_ms = l0.elapsed_time(l1) / steps
 
     nbytes = (algorithmic_bytes_fp8 if fp8 else algorithmic_bytes)(inp.seqlens, w.s_q, w.h_q)
     flops = algorithmic_flops(inp.seqlens, w.s_q, w.h_q, w.causal)
     gbps = nbytes / (ms_step * 1e-3) / 1e9
     tflops = flops / (ms_step * 1e-3) / 1e12
+    # one layer = the attention call (decode + combine), without the plan,
+    # which a decode step builds once for all its layers
+    layer_s = layer_ms * 1e-3
     # roofline of the dominant kernel (the decode kernel): algorithmic bytes
     # or FLOPs of one call over that kernel's mean event-timed duration
     dec_gbps = nbytes / (dec_ms * 1e-3) / 1e9
@@ -298,6 +317,16 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
         "metadata_us_median": round(float(np.median(meta_ms)) * 1e3, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 2),
         "combine_kernel_us": round(comb_ms * 1e3, 2),
+        "layer": {"what": "one attention call per layer (decode + combine kernels) with a plan built "
+                          "once, back to back between two events; the per-step plan is timed apart "
+                          "(metadata_us_median)",
+                  "us": round(layer_ms * 1e3, 2),
+                  "gbps": round(nbytes / layer_s / 1e9, 1), "tflops": round(flops / layer_s / 1e12, 2),
+                  "hbm_frac": round(nbytes / layer_s / 1e9 / MI355X_HBM_GBPS, 4),
+                  "mfma_frac": round(flops / layer_s / 1e12 / MI355X_BF16_TFLOPS, 4)},
+        "roofline_kernel": KERNEL_NAMES.get((fp8, w.h_q * w.s_q >= 64), "decode"),
+        "roofline_scope": "the decode kernel alone: algorithmic bytes (or FLOPs) of one call over its "
+                          "mean event-timed duration",
         "algorithmic_bytes": nbytes,
         "algorithmic_flops": flops,
         "kv_copies_rotated": copies,
@@ -314,6 +343,22 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
     if cpu_budget > 0:
         line["cpu_baseline"] = cpu_baseline(name, inp, cpu_budget)
     return line
+
+
+# the decode kernel the roofline is taken on, by (FP8 cache, >= 64 rows)
+KERNEL_NAMES = {(False, False): "mla_decode_rows16_kernel", (False, True): "mla_decode_ws_kernel",
+                (True, False): "mla_decode_rows16_fp8_kernel", (True, True): "mla_decode_rows16_fp8_kernel"}
+
+
+def workload_summary(line: dict) -> dict:
+    """The figures of one workload's bench line that go into the headline
+    line's `workloads` object."""
+    keys = ("ms_per_step", "value", "tflops", "hbm_frac_of_peak", "mfma_frac_of_peak", "decode_kernel_us",
+            "combine_kernel_us", "metadata_us_median", "decode_call_us", "layer", "roofline",
+            "roofline_kernel", "counters", "algorithmic_bytes", "algorithmic_flops")
+    out = {k: line[k] for k in keys if k in line}
+    out["config"] = line["config"]["workload"]
+    return out
 
 
 _SLEEP_CYCLES_PER_MS = None
@@ -351,11 +396,13 @@ def append_bytes(inp, fp8: bool = False) -> int:
     return (1152 + (644 if fp8 else 1152)) * rows + 4 * pages + 4 * inp.batch
 
 
-def run_append(name: str, steps: int, warmup: int, fp8: bool = False):
+def run_append(name: str, steps: int, warmup: int, fp8: bool = False, rotate_bytes: int = 1 << 30):
     """One step = one mla_kv_append call on the workload's new rows. Each call
     writes the same rows (idempotent), timed call by call with HIP events on
     the launch stream, behind a device-side spin that keeps the host's launch
-    cost out of the events."""
+    cost out of the events. The cache and the new rows are replicated so
+    consecutive calls use different copies (>= rotate_bytes in rotation), so
+    no call finds the previous one's rows or pages in the 256 MB MALL."""
     import torch
     import mla_paged_kv_02_amd as mla
 
@@ -374,24 +421,27 @@ def run_append(name: str, steps: int, warmup: int, fp8: bool = False):
     new = to_dev(inp.new_bits)
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seqlens).to(dev)
+    set_bytes = kv.numel() * kv.element_size() + new.numel() * new.element_size()
+    copies = max(1, min(64, math.ceil(rotate_bytes / set_bytes)))
+    sets = [(new, kv)] + [(new.clone(), kv.clone()) for _ in range(copies - 1)]
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        append(new, sl, bt, kv)
+    for i in range(warmup):
+        append(sets[i % copies][0], sl, bt, sets[i % copies][1])
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     hold_queue(0.1 * steps)
     t0.record(stream)
-    for _ in range(steps):
-        append(new, sl, bt, kv)
+    for i in range(steps):
+        append(sets[i % copies][0], sl, bt, sets[i % copies][1])
     t1.record(stream)
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     hold_queue(0.1 * steps)
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record(stream)
-        append(new, sl, bt, kv)
+        append(sets[i % copies][0], sl, bt, sets[i % copies][1])
         b.record(stream)
     torch.cuda.synchronize()
     call_ms = np.array([a.elapsed_time(b) for a, b in evs])
@@ -415,6 +465,7 @@ def run_append(name: str, steps: int, warmup: int, fp8: bool = False):
                                f"final lengths U[{w['lengths'][2]},{w['lengths'][3]}], rows of 576 bf16, page 64",
                    "batch": inp.batch, "s_new": inp.s_new, "seed": w["seed"]},
         "append_kernel_us_avg": round(ms_step * 1e3, 2),
+        "copies_rotated": copies,
         "append_call_us_median": round(float(np.median(call_ms)) * 1e3, 2),
         "append_call_us_min": round(float(call_ms.min()) * 1e3, 2),
         "append_call_us_p90": round(float(np.percentile(call_ms, 90)) * 1e3, 2),
@@ -749,6 +800,9 @@ def main():
     ap.add_argument("--ingest-mfma", metavar="MFMA_DIR",
                     help="rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 output dir: add the MFMA op count "
                          "to profiles/hbm_traffic.json for --workload (no GPU needed)")
+    ap.add_argument("--only", action="store_true",
+                    help="decode: time only --workload (by default the memory-bound line also carries "
+                         "every other workload under 'workloads')")
     ap.add_argument("--no-stream-context", action="store_true",
                     help="skip the torch streaming-read / copy bandwidth context")
     ap.add_argument("--kernel", default="mla_decode_rows16_kernel",
@@ -793,21 +847,34 @@ def main():
     if args.op in ("kv_append", "kv_append_fp8"):
         names = list(APPEND_WORKLOADS) if args.workload in ("all", DEFAULT_WORKLOAD) else [args.workload]
         for name in names:
-            print(json.dumps(run_append(name, args.steps, args.warmup, fp8=args.op == "kv_append_fp8")),
-                  flush=True)
+            print(json.dumps(run_append(name, args.steps, args.warmup, fp8=args.op == "kv_append_fp8",
+                                        rotate_bytes=int(args.rotate_gib * (1 << 30)))), flush=True)
         return
     fp8 = args.op == "decode_fp8"
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     if fp8:
         names = [n for n in names if WORKLOADS[n].h_q * WORKLOADS[n].s_q <= 64]
     ctx = None if args.no_stream_context else streaming_context()
+    rotate = int(args.rotate_gib * (1 << 30))
     for name in names:
         line = run_workload(name, args.steps, args.warmup,
                             args.cpu_budget if (name == DEFAULT_WORKLOAD or args.workload != "all") and not fp8
                             else 0,
-                            int(args.rotate_gib * (1 << 30)), args.num_partitions, fp8=fp8)
+                            rotate, args.num_partitions, fp8=fp8)
         if ctx:
             line["achievable_context"] = ctx
+        if args.workload == DEFAULT_WORKLOAD and not args.only:
+            # the other workloads, timed the same way, in the same line: the
+            # 128-head ones carry the MFMA half of the metric
+            import torch
+            others = {}
+            for other in WORKLOADS:
+                if other == name or (fp8 and WORKLOADS[other].h_q * WORKLOADS[other].s_q > 64):
+                    continue
+                torch.cuda.empty_cache()
+                others[other] = workload_summary(run_workload(other, args.steps, args.warmup, 0, rotate,
+                                                              args.num_partitions, fp8=fp8))
+            line["workloads"] = {name: workload_summary(line), **others}
         print(json.dumps(line), flush=True)
 
 
