@@ -800,6 +800,10 @@ def main():
     ap.add_argument("--ingest-mfma", metavar="MFMA_DIR",
                     help="rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 output dir: add the MFMA op count "
                          "to profiles/hbm_traffic.json for --workload (no GPU needed)")
+    ap.add_argument("--decode-kernel", default=None, choices=("rows16", "ws"),
+                    help="force one decode organisation for BF16 plans (mla_set_plan_override)")
+    ap.add_argument("--merge", default=None, choices=("kernel", "fused"),
+                    help="force where split sequences are merged (mla_set_plan_override)")
     ap.add_argument("--only", action="store_true",
                     help="decode: time only --workload (by default the memory-bound line also carries "
                          "every other workload under 'workloads')")
@@ -851,6 +855,9 @@ def main():
                                         rotate_bytes=int(args.rotate_gib * (1 << 30)))), flush=True)
         return
     fp8 = args.op == "decode_fp8"
+    if args.decode_kernel or args.merge:
+        import mla_paged_kv_02_amd as mla
+        mla.set_plan_override(kernel=args.decode_kernel, merge=args.merge)
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     if fp8:
         names = [n for n in names if WORKLOADS[n].h_q * WORKLOADS[n].s_q <= 64]

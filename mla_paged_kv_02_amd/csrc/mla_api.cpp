@@ -113,7 +113,9 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     const int ov = g_kernel_override.load(std::memory_order_relaxed);
     if (ov == 0 && !fp8) k = DecodeKernel::Rows16;
     if (ov == 1 && !fp8) k = DecodeKernel::WaveSplit;
-    const int tm = k == DecodeKernel::Rows16 ? 16 : 64;
+    // the score/value-wave kernel's block: the smallest of 16, 32 and 64
+    // rows that holds the sequence's rows, 64 beyond
+    const int tm = k == DecodeKernel::Rows16 ? 16 : pl.M <= 16 ? 16 : pl.M <= 32 ? 32 : 64;
     pl.kernel = k;
     pl.tm = tm;
     pl.R = (pl.M + tm - 1) / tm;
@@ -126,7 +128,7 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
         // more than its share), and a quarter fewer 128 KB FP32 partials
         // shortens the combine (4 sequences of 1K-64K tokens at 64 heads:
         // call 53.4 vs 55.5 us, decode kernel unchanged).
-        if (k == DecodeKernel::WaveSplit && pl.R == 1) p = cus * 3 / 4;
+        if (k == DecodeKernel::WaveSplit && tm == 64 && pl.R == 1) p = cus * 3 / 4;
         if (p < 1) p = 1;
     }
     pl.P = (p + 7) / 8 * 8;  // whole groups of 8 for the XCD-aware block mapping

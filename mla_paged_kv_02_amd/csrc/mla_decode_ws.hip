@@ -1,5 +1,5 @@
-// mla_decode_ws.hip - split-KV MLA decode for blocks of 64 query rows with
-// separate score and value waves.
+// mla_decode_ws.hip - split-KV MLA decode for blocks of 16, 32 or 64 query
+// rows with separate score and value waves.
 //
 // Method as in the other decode kernels (page "MLA 和 MHA 的 Kernel 区别",
 // section "MLA 的 FlashAttention": stream latent-cache tiles through on-chip
@@ -7,22 +7,27 @@
 // form). This organisation is for query blocks wide enough that the two
 // products and the LDS traffic that feeds them are the work:
 //
-//  * eight waves, two per SIMD. Score wave s owns key tile s & 1 (keys
-//    16(s&1)..+15 of every half page) for the 32 query rows of row tiles
-//    2(s>>1) and 2(s>>1)+1 (query in registers): each K fragment it reads
-//    from LDS feeds two row tiles. It computes S^T = K Q^T, the mask and the
-//    softmax weights of its keys. Value waves 4..7 own output columns
-//    128v..128v+127 of all 64 rows (O^T accumulators) and compute
+//  * score waves own key tiles (16 keys of a 32-key half page). For 64-row
+//    blocks there are four, two per key tile, each holding the query of two
+//    row tiles in registers, so each K fragment read from LDS feeds two row
+//    tiles; for 16- and 32-row blocks two, one per key tile, each holding
+//    all the block's rows. They compute S^T = K Q^T, the mask and the
+//    softmax weights of their keys. Four value waves own output columns
+//    128v..128v+127 of all the block's rows (O^T accumulators) and compute
 //    O^T += V^T P^T. P crosses over through LDS in exactly the MFMA operand
-//    layout, so each V^T fragment (two transposing LDS reads) feeds four row
-//    tiles instead of one. While a score wave waits on LDS or runs its exps,
-//    the value wave on the same SIMD keeps the matrix core busy;
+//    layout, so each V^T fragment (two transposing LDS reads) feeds every
+//    row tile. While a score wave waits on LDS or runs its exps, the value
+//    wave on the same SIMD keeps the matrix core busy;
 //  * the cache streams through a ring of four half-page slots (32 keys,
 //    36 KB): the value waves load them with 16-byte direct loads, two half
 //    pages ahead. Step c scores half page c and accumulates half page c-1;
 //    one workgroup barrier per step publishes half page c, the weights of
 //    half page c-1 and the overflow flags, and frees the slot the value
-//    waves finished;
+//    waves finished. The stream is the partition's whole page list: the
+//    last steps of a segment load the first two half pages of the
+//    partition's next segment, which therefore starts without a fill (its
+//    half pages sit two slots further on, so a segment's slots are offset
+//    by 0 or 2);
 //  * the softmax reference of each row is fixed at its maximum over the
 //    first half page of the segment plus a margin: on that half page the
 //    score waves score both key tiles, so the two waves of a row pair take
@@ -52,7 +57,14 @@ __device__ __forceinline__ int ld_const_ws(const int32_t* p, size_t i) {
         reinterpret_cast<uintptr_t>(p))[i];
 }
 
-constexpr int kScoreWaves = 4;
+// block of 16 kRT rows: score waves, threads, row tiles of a score wave
+template <int kRT>
+struct WsShape {
+    static constexpr int kScoreWaves = kRT == 4 ? 4 : 2;
+    static constexpr int kThreads = 64 * (kScoreWaves + 4);
+    static constexpr int kRows = 16 * kRT;
+    static constexpr int NR = kRT == 1 ? 1 : 2;
+};
 constexpr int kCRows = 32;                      // keys per ring slot (half page)
 constexpr int kCBytes = kCRows * kRowBytes;     // 36864
 constexpr int kWLoads = 9;                      // a value wave's wave-loads per slot (8 rows)
@@ -84,33 +96,37 @@ __device__ __forceinline__ void block_barrier() {
 
 }  // namespace
 
-__global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[kCBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[kCBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[kCBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[kCBytes];
+template <int kRT>
+__global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(DecodeArgs a) {
+    using Sh = WsShape<kRT>;
+    constexpr int kRows = Sh::kRows;
+    constexpr int kSW = Sh::kScoreWaves;
+    constexpr int kPBytes = kRT * 1024;
+
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * kCBytes];
     // weights of a half page for the value waves: row tile rt at 1 KB * rt,
     // lane l at 16 l (the B operand of O^T += V^T P^T); two buffers by parity
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][4 * 1024];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kPBytes];
     // per row of the block: softmax reference, and the sums of the two key
     // tiles, for the epilogue
-    __shared__ float row_m[64];
-    __shared__ float row_l[2][64];
+    __shared__ float row_m[kRows];
+    __shared__ float row_l[2][kRows];
     // overflow flags by step parity: set during step c in flag[c & 1], read
     // by every wave after the next barrier
     __shared__ int restart_flag[2];
     __shared__ int last_flag;   // this workgroup merges a split sequence
 
+    if (!plan_matches_or_poison<Sh::kThreads>(a)) return;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const bool scorer = wid < kScoreWaves;
-    // score wave sw: key tile sw & 1 of row pair sw >> 1; value wave sw:
-    // column block sw (and rows 8 sw..8 sw+7 of every half page it loads)
-    const int sw = wid & 3;
+    const bool scorer = wid < kSW;
+    // score wave sw: key tile sw & 1 (of row pair sw >> 1 for 64-row
+    // blocks); value wave sw: column block sw (and rows 8 sw..8 sw+7 of
+    // every half page it loads)
+    const int sw = scorer ? wid : wid - kSW;
     const int g = lane >> 4;
     const int i16 = lane & 15;
 
-    if (!plan_matches_or_poison<512>(a)) return;
     const int bid = blockIdx.x;
     const int rb = (bid >> 3) % a.R;
     const int p = ((bid >> 3) / a.R) * 8 + (bid & 7);
@@ -129,10 +145,26 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
         restart_flag[0] = 0;
         restart_flag[1] = 0;
     }
-    uint8_t* const slots[4] = {ring0, ring1, ring2, ring3};
-    const uint32_t slot_lds[4] = {lds_addr_of(ring0), lds_addr_of(ring1), lds_addr_of(ring2),
-                                  lds_addr_of(ring3)};
+    const uint32_t ring_lds = lds_addr_of(ring);
 
+    // The partition's segments: (sequence, page range) in order, each
+    // holding at least one page; b < 0 past the partition's end.
+    struct Seg {
+        int b, lo, hi, nseq;
+    };
+    auto find_seg = [&](int b, int n) {
+        while (b < b_end || (b == b_end && n < n_end)) {
+            const int nseq = b == b0 ? len0 : ld_const_ws(a.seqlens, b);
+            const int hi = (b == b_end) ? n_end : pages_of(nseq);
+            if (n < hi) return Seg{b, n, hi, nseq};
+            ++b;
+            n = 0;
+        }
+        return Seg{-1, 0, 0, 0};
+    };
+
+    // ---- value waves: the fetch stream, the partition's half pages in
+    // order. fseg/fc name the next half page to take; fpage is its page.
     // value wave v gathers rows 8v..8v+7 of every half page: LDS 16-byte
     // chunk k of its 9 KB holds row k/72, slot k%72 = logical chunk
     // slot^swz(row); goff[j] is the lane's source offset for load j
@@ -144,14 +176,41 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
         const int c = k - r * kRowChunks;
         goff[j] = r * kRowBytes + ((c ^ lds_swizzle(r)) << 4);
     }
-    // Load j (of kWLoads) of this value wave's part of a half page. Rows at
-    // or past the sequence end read the page's first kilobyte (row 0, always
+    Seg fseg = find_seg(b0, n0);
+    int fc = 0;
+    auto fpage_of = [&]() {
+        const int32_t* bt_row = a.block_table + (size_t)fseg.b * a.max_blocks;
+        return reinterpret_cast<const uint8_t*>(a.kv) + (size_t)ld_const_ws(bt_row, fseg.lo + fc / 2) * kPageBytes;
+    };
+    const uint8_t* fpage = nullptr;
+    // the half page taken for issue: its page, which half, and the rows of
+    // the page that hold tokens
+    const uint8_t* t_src = nullptr;
+    int t_half = 0, t_rows = 0;
+    auto take = [&]() -> bool {
+        if (fseg.b < 0) return false;
+        t_src = fpage;
+        t_half = fc & 1;
+        t_rows = fseg.nseq - (fseg.lo + fc / 2) * kPageRows;
+        if (++fc == 2 * (fseg.hi - fseg.lo)) {
+            fseg = find_seg(fseg.b + 1, 0);
+            fc = 0;
+        }
+        if (fseg.b >= 0 && (fc & 1) == 0) fpage = fpage_of();
+        return true;
+    };
+    // load j of the taken half page into the slot at `dst`. Rows at or past
+    // the sequence end read the page's first kilobyte (row 0, always
     // valid): finite data whose softmax weight is zero.
-    auto issue_one = [&](const uint8_t* page, int half, int valid, uint32_t dst, int j) {
-        const int base = half * kCBytes + sw * 9216;
-        const int r = half * kCRows + sw * 8 + (j * 64 + lane) / kRowChunks;
-        const uint32_t off = r < valid ? (uint32_t)(base + goff[j]) : (uint32_t)(lane * 16);
-        load_lds16_untracked(page, off, dst + sw * 9216 + j * 1024);
+    auto issue_one = [&](uint32_t dst, int j) {
+        const int base = t_half * kCBytes + sw * 9216;
+        const int r = t_half * kCRows + sw * 8 + (j * 64 + lane) / kRowChunks;
+        const uint32_t off = r < t_rows ? (uint32_t)(base + goff[j]) : (uint32_t)(lane * 16);
+        load_lds16_untracked(t_src, off, dst + sw * 9216 + j * 1024);
+    };
+    auto issue_all = [&](uint32_t dst) {
+#pragma unroll
+        for (int j = 0; j < kWLoads; ++j) issue_one(dst, j);
     };
 
     // per-lane LDS offsets inside a slot: K fragment of k-step ks for key row
@@ -172,46 +231,36 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
     // waves' accumulators never live at the same program point.
     auto run = [&](auto role) {
         constexpr bool kScorer = decltype(role)::value;
-        // score wave: key tile kt, block rows lrow[r] = 32 rp + 16 r + i16
-        constexpr int NR = kScorer ? 2 : 1;
+        // score wave: key tile kt, block rows lrow[r] = 16 (rt0 + r) + i16
+        constexpr int NR = kScorer ? Sh::NR : 1;
         const int kt = sw & 1;
-        const int rp = sw >> 1;
+        const int rt0 = kRT == 4 ? 2 * (sw >> 1) : 0;
         int lrow[NR], stok[NR];
         bool srow_ok[NR];
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            lrow[r] = 32 * rp + 16 * r + i16;
-            srow_ok[r] = rb * 64 + lrow[r] < a.M;
-            stok[r] = srow_ok[r] ? (rb * 64 + lrow[r]) / a.h_q : 0;
+            lrow[r] = 16 * (rt0 + r) + i16;
+            srow_ok[r] = rb * kRows + lrow[r] < a.M;
+            stok[r] = srow_ok[r] ? (rb * kRows + lrow[r]) / a.h_q : 0;
         }
         bf16x8 qf[NR][kScorer ? kKS : 1];
-        f32x4 o[kScorer ? 1 : 4][kScorer ? 1 : kVTiles];
+        f32x4 o[kScorer ? 1 : kRT][kScorer ? 1 : kVTiles];
 
-        int b = b0, n = n0;
-        while (b < b_end || (b == b_end && n < n_end)) {
-            const int nseq = b == b0 ? len0 : ld_const_ws(a.seqlens, b);
+        // value waves: the stream's first two half pages
+        bool issued_next = false;   // the half page after the one waited for is in flight
+        if constexpr (!kScorer) {
+            if (fseg.b >= 0) fpage = fpage_of();
+            if (take()) issue_all(ring_lds);
+            issued_next = take();
+            if (issued_next) issue_all(ring_lds + kCBytes);
+        }
+        int soff = 0;   // ring slot of the segment's first half page (0 or 2)
+
+        Seg seg = find_seg(b0, n0);
+        while (seg.b >= 0) {
+            const int b = seg.b, lo = seg.lo, hi = seg.hi, nseq = seg.nseq;
             const int npages = pages_of(nseq);
-            const int hi = (b == b_end) ? n_end : npages;
-            if (n >= hi) { ++b; n = 0; continue; }
-            const int lo = n;
             const int nch = 2 * (hi - lo);   // half pages of the segment
-
-            const int32_t* bt_row = a.block_table + (size_t)b * a.max_blocks;
-            auto page_of_chunk = [&](int c) {
-                const int pn = lo + (c < nch ? c : nch - 1) / 2;
-                return reinterpret_cast<const uint8_t*>(a.kv) +
-                       (size_t)ld_const_ws(bt_row, pn) * kPageBytes;
-            };
-            // load j of half page c (past the segment end: the last one again,
-            // so that every step issues the same number of loads)
-            auto issue_part = [&](int c, const uint8_t* page, uint32_t dst, int j) {
-                const int cc = c < nch ? c : nch - 1;
-                issue_one(page, cc & 1, nseq - (lo + cc / 2) * kPageRows, dst, j);
-            };
-            auto issue_chunk = [&](int c, const uint8_t* page, uint32_t dst) {
-#pragma unroll
-                for (int j = 0; j < kWLoads; ++j) issue_part(c, page, dst, j);
-            };
 
             int L[NR];
             float m_ref[NR], l_run[NR];
@@ -230,7 +279,7 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < NR; ++r) {
                     const uint16_t* qp = a.q +
-                        ((size_t)b * a.M + (srow_ok[r] ? rb * 64 + lrow[r] : rb * 64)) * kHeadDim + g * 8;
+                        ((size_t)b * a.M + (srow_ok[r] ? rb * kRows + lrow[r] : rb * kRows)) * kHeadDim + g * 8;
 #pragma unroll
                     for (int ks = 0; ks < kKS; ++ks) qf[r][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
                 }
@@ -238,16 +287,9 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 
             bool restart = false;
             do {
-                // value waves fill slots 0 and 1; the score waves' query
-                // loads are the compiler's own and waited for where used
-                const uint8_t* page2 = nullptr;
                 if constexpr (!kScorer) {
-                    issue_chunk(0, page_of_chunk(0), slot_lds[0]);
-                    issue_chunk(1, page_of_chunk(1), slot_lds[1]);
-                    page2 = page_of_chunk(2);
-                    wait_then_fence<kWaitAll>();
 #pragma unroll
-                    for (int rt = 0; rt < 4; ++rt)
+                    for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
                         for (int t = 0; t < kVTiles; ++t) o[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
                 } else {
@@ -261,36 +303,39 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
                 bool skip = false;   // overflow seen: no more weights until the restart
 
-                // Step c: the value waves issue half page c+2 into slot
-                // (S+2) % 4 (its previous contents, half page c-2, were
-                // accumulated in step c-1) and accumulate half page c-1 from
-                // slot (S+3) % 4, while the score waves turn half page c
-                // (slot S = c % 4) into weights.
+                // Step c: the value waves take the stream's next half page (this
+                // segment's half page c+2, or the next segment's first two) into
+                // slot (soff+c+2) % 4 (its previous contents, half page c-2, were
+                // accumulated in step c-1) and accumulate half page c-1 from slot
+                // (soff+c+3) % 4, while the score waves turn half page c (slot
+                // (soff+c) % 4) into weights. The last step, c = nch, only
+                // accumulates.
                 int c = 0;
                 auto step = [&](auto sc) -> bool {
                     constexpr int S = decltype(sc)::value;
-                    const uint8_t* page_next = nullptr;
+                    const uint8_t* slot_cur = ring + ((S + soff) & 3) * kCBytes;
                     if constexpr (!kScorer) {
-                        wait_then_fence<kWaitSlot>();   // my part of half page c
-                        page_next = page_of_chunk(c + 3);
+                        // my part of half page c (at most the next one's loads are younger)
+                        if (c < nch) {
+                            if (issued_next) wait_then_fence<kWaitSlot>();
+                            else wait_then_fence<kWaitAll>();
+                        }
                     }
                     block_barrier();   // publishes the weights and flags of step c-1
                     if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
-                    // value waves: half page c+2 into slot (S+2) % 4, which held
-                    // half page c-2 (accumulated in step c-1); spread over the
-                    // value products below, so the address unit that takes
-                    // the loads never backs the wave up for long
-                    const uint8_t* const page_c2 = page2;
+                    bool issue_now = false;
+                    uint32_t dst = 0;
                     if constexpr (!kScorer) {
-                        page2 = page_next;
-                        if (c == 0) issue_chunk(c + 2, page_c2, slot_lds[(S + 2) % 4]);
+                        issue_now = c < nch && take();
+                        dst = ring_lds + ((S + soff + 2) & 3) * kCBytes;
+                        if (c == 0 && issue_now) issue_all(dst);
                     } else if (c < nch) {
                         // ---- S^T = K Q^T for key tile `tile` of half page c,
-                        // both row tiles; one K fragment feeds both. Lane
-                        // holds keys key0 + j (j < 4) of rows lrow[r], -inf
-                        // where masked; lm[r] = the lane's maximum of them.
+                        // every row tile of this wave; one K fragment feeds them
+                        // all. Lane holds keys key0 + j (j < 4) of rows lrow[r],
+                        // -inf where masked; lm[r] = the lane's maximum of them.
                         auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&lm)[NR]) {
-                            const uint8_t* kb = slots[S] + tile * 16 * kRowBytes;
+                            const uint8_t* kb = slot_cur + tile * 16 * kRowBytes;
                             f32x4 sp[NR][2];
 #pragma unroll
                             for (int r = 0; r < NR; ++r)
@@ -369,20 +414,20 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                                     pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r][j], a.scale_log2, neg_m));
                                     l_run[r] += pw[j];
                                 }
-                                // B = P^T of row tile 2 rp + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j
-                                *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(2 * rp + r) * 1024 + lane * 16 + kt * 8]) =
+                                // B = P^T of row tile rt0 + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j
+                                *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(rt0 + r) * 1024 + lane * 16 + kt * 8]) =
                                     pack_bf16x4(pw);
                             }
                         }
                     }
                     if (!kScorer && c >= 1) {
-                        // ---- O^T += V^T P^T for half page c-1: four row tiles
+                        // ---- O^T += V^T P^T for half page c-1: the row tiles
                         // share each V^T fragment (two transposing reads)
-                        const uint8_t* cur = slots[(S + 3) % 4];
+                        const uint8_t* cur = ring + ((S + soff + 3) & 3) * kCBytes;
                         const uint8_t* pb = &pbuf[(S + 1) & 1][lane * 16];
-                        bf16x8 pf[4];
+                        bf16x8 pf[kRT];
 #pragma unroll
-                        for (int rt = 0; rt < 4; ++rt) pf[rt] = lds_read16(pb + rt * 1024);
+                        for (int rt = 0; rt < kRT; ++rt) pf[rt] = lds_read16(pb + rt * 1024);
                         constexpr int VD = 5;
                         auto v_frag = [&](int t) {
                             const int dt = sw * kVTiles + t;
@@ -395,13 +440,16 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
 #pragma unroll
                         for (int t = 0; t < kVTiles; ++t) {
 #pragma unroll
-                            for (int rt = 0; rt < 4; ++rt) o[rt][t] = mfma16(vf[t % VD], pf[rt], o[rt][t]);
+                            for (int rt = 0; rt < kRT; ++rt) o[rt][t] = mfma16(vf[t % VD], pf[rt], o[rt][t]);
                             if (t + VD < kVTiles) vf[t % VD] = v_frag(t + VD);
-                            issue_part(c + 2, page_c2, slot_lds[(S + 2) % 4], t);
+                            if (issue_now) issue_one(dst, t);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                         static_assert(kVTiles + 1 == kWLoads, "one load per value tile and one after");
-                        issue_part(c + 2, page_c2, slot_lds[(S + 2) % 4], kVTiles);
+                        if (issue_now) issue_one(dst, kVTiles);
+                    }
+                    if constexpr (!kScorer) {
+                        if (c < nch) issued_next = issue_now;
                     }
                     ++c;
                     return c <= nch;
@@ -412,9 +460,9 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 using S3 = std::integral_constant<int, 3>;
                 while (step(S0{}) && step(S1{}) && step(S2{}) && step(S3{})) {
                 }
-                // drain the half pages still in flight; after the barrier
-                // every wave sees an overflow raised in the last step too
-                wait_then_fence<kWaitAll>();
+                // after the barrier every wave sees an overflow raised in the
+                // last step too (the next segment's first half pages stay in
+                // flight)
                 block_barrier();
                 restart = (restart_flag[0] | restart_flag[1]) != 0;
                 if (restart) {
@@ -439,6 +487,15 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                     if constexpr (kScorer) {
 #pragma unroll
                         for (int r = 0; r < NR; ++r) m_ref[r] = row_m[lrow[r]];
+                    } else {
+                        // drain the ring and refill it from this segment's start
+                        wait_then_fence<kWaitAll>();
+                        fseg = seg;
+                        fc = 0;
+                        fpage = fpage_of();
+                        if (take()) issue_all(ring_lds + soff * kCBytes);
+                        issued_next = take();
+                        if (issued_next) issue_all(ring_lds + (soff + 1) * kCBytes);
                     }
                     block_barrier();   // every wave has read the flags and row_m
                 }
@@ -460,8 +517,8 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
             if constexpr (!kScorer) {
                 const int col0 = sw * 128 + 4 * g;   // tile t covers columns col0 + 16 t .. +3
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const int row = rb * 64 + rt * 16 + i16;
+                for (int rt = 0; rt < kRT; ++rt) {
+                    const int row = rb * kRows + rt * 16 + i16;
                     const float lsum = row_l[0][rt * 16 + i16] + row_l[1][rt * 16 + i16];
                     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
                     if (row >= a.M) continue;
@@ -496,19 +553,31 @@ __global__ __launch_bounds__(512) void mla_decode_ws_kernel(DecodeArgs a) {
                 }
             }
             block_barrier();   // row_m, row_l and the buffers are free again
-            if (!full && a.counters) count_partial_and_combine<512, 64>(a, b, rb, &last_flag);
-            ++b;
-            n = 0;
+            if (!full && a.counters)
+                count_partial_and_combine<Sh::kThreads, kRows, (kRT == 4 ? 512 : 256)>(a, b, rb, &last_flag);
+            soff = (soff + nch) & 3;
+            seg = find_seg(b + 1, 0);
         }
-        if (a.counters) write_empty_sequences<512>(a);
+        if (a.counters) write_empty_sequences<Sh::kThreads>(a);
     };
     if (scorer) run(std::true_type{});
     else run(std::false_type{});
 }
 
-hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
-    hipLaunchKernelGGL(mla_decode_ws_kernel, dim3(plan.P * plan.R), dim3(512), 0, stream, args);
+template <int kRT>
+static hipError_t launch_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
+    hipLaunchKernelGGL(mla_decode_ws_kernel<kRT>, dim3(plan.P * plan.R), dim3(WsShape<kRT>::kThreads), 0, stream,
+                       args);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
+    switch (plan.tm) {
+        case 16: return launch_ws<1>(plan, args, stream);
+        case 32: return launch_ws<2>(plan, args, stream);
+        case 64: return launch_ws<4>(plan, args, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mla

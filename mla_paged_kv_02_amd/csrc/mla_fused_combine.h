@@ -86,8 +86,10 @@ __device__ __forceinline__ void combine_rows(const DecodeArgs& a, int b, int row
 
 // After this workgroup stored its partial for (b, rb): count it, and merge
 // the sequence's partials when it is the last. `flag` is an int in LDS that
-// no wave touches around the call. Every thread calls it.
-template <int kThreads, int kRows>
+// no wave touches around the call. Every thread calls it; the first
+// kMergeThreads of them (a multiple of kRows dividing 512 columns evenly)
+// do the merge.
+template <int kThreads, int kRows, int kMergeThreads = kThreads>
 __device__ __forceinline__ void count_partial_and_combine(const DecodeArgs& a, int b, int rb, int* flag) {
     const int32_t* si = a.meta + kMetaHeader + kPartInts * a.P + 4 * b;
     const int base = si[0];
@@ -101,7 +103,8 @@ __device__ __forceinline__ void count_partial_and_combine(const DecodeArgs& a, i
     __syncthreads();   // every wave has read the flag before it is reused
     if (!last) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // no stale copies of the partials
-    combine_rows<kThreads, kRows>(a, b, rb * kRows, base, cnt);
+    if (kMergeThreads == kThreads || threadIdx.x < kMergeThreads)
+        combine_rows<kMergeThreads, kRows>(a, b, rb * kRows, base, cnt);
     if (threadIdx.x == 0) __hip_atomic_store(&a.counters[b * a.R + rb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

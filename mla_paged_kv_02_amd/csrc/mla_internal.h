@@ -11,8 +11,9 @@ namespace mla {
 // the M = h_q*s_q rows of a sequence, P partitions cut the page list, and
 // the grid is P*R workgroups.
 //   Rows16:    tm = 16, four waves each owning a key stripe of every page;
-//   WaveSplit: tm = 64, four score waves and four value waves;
+//   WaveSplit: tm = 16, 32 or 64, score waves and four value waves;
 //   Rows16Fp8: the Rows16 organisation over the FP8 page format.
+// WaveSplit blocks hold 16, 32 or 64 rows (tm).
 enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8 };
 
 struct Plan {

@@ -297,9 +297,9 @@ def test_plan_override_is_checked_and_shapes_the_plan():
     assert lib.mla_set_plan_override(-1, -2) == INVALID
     lens = [300, 70, 129, 5000]
     try:
-        assert lib.mla_set_plan_override(1, -1) == OK          # 64-row blocks at 16 rows: R = 1
+        assert lib.mla_set_plan_override(1, -1) == OK          # 32-row score/value blocks at 32 rows: R = 1
         ws_plan = _host_plan(lens, 32, 1, 64)
-        assert ws_plan[8] == 1
+        assert ws_plan[8] == 1 and ws_plan[3] == 3
         assert lib.mla_set_plan_override(0, -1) == OK          # 16-row blocks at 64 rows: R = 4
         r16_plan = _host_plan(lens, 64, 1, 64)
         assert r16_plan[8] == 4
