@@ -324,7 +324,7 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
                   "gbps": round(nbytes / layer_s / 1e9, 1), "tflops": round(flops / layer_s / 1e12, 2),
                   "hbm_frac": round(nbytes / layer_s / 1e9 / MI355X_HBM_GBPS, 4),
                   "mfma_frac": round(flops / layer_s / 1e12 / MI355X_BF16_TFLOPS, 4)},
-        "roofline_kernel": KERNEL_NAMES.get((fp8, w.h_q * w.s_q >= 64), "decode"),
+        "roofline_kernel": decode_kernel_name(fp8, w.h_q * w.s_q),
         "roofline_scope": "the decode kernel alone: algorithmic bytes (or FLOPs) of one call over its "
                           "mean event-timed duration",
         "algorithmic_bytes": nbytes,
@@ -346,8 +346,20 @@ def run_workload(name: str, steps: int, warmup: int, cpu_budget: float, rotate_b
 
 
 # the decode kernel the roofline is taken on, by (FP8 cache, >= 64 rows)
-KERNEL_NAMES = {(False, False): "mla_decode_rows16_kernel", (False, True): "mla_decode_ws_kernel",
-                (True, False): "mla_decode_rows16_fp8_kernel", (True, True): "mla_decode_rows16_fp8_kernel"}
+# the decode organisation forced with --decode-kernel (None: the plan's own choice)
+FORCED_KERNEL = None
+
+
+def decode_kernel_name(fp8: bool, rows: int) -> str:
+    """The decode kernel a plan of `rows` query rows per sequence runs: the
+    library picks 16-row blocks below 64 rows and 64-row score/value blocks
+    from there (--decode-kernel forces one); the FP8 cache has the 16-row
+    kernel only."""
+    if fp8:
+        return "mla_decode_rows16_fp8_kernel"
+    kind = FORCED_KERNEL or ("rows16" if rows < 64 else "ws")
+    return {"rows16": "mla_decode_rows16_kernel", "ws": "mla_decode_ws_kernel",
+            "fw": "mla_decode_fw_kernel"}[kind]
 
 
 def workload_summary(line: dict) -> dict:
@@ -777,6 +789,7 @@ def summarize_trace(trace_dir: str, command: str, bench_log: str = "", op: str =
 
 
 def main():
+    global FORCED_KERNEL
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -800,7 +813,7 @@ def main():
     ap.add_argument("--ingest-mfma", metavar="MFMA_DIR",
                     help="rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 output dir: add the MFMA op count "
                          "to profiles/hbm_traffic.json for --workload (no GPU needed)")
-    ap.add_argument("--decode-kernel", default=None, choices=("rows16", "ws"),
+    ap.add_argument("--decode-kernel", default=None, choices=("rows16", "ws", "fw"),
                     help="force one decode organisation for BF16 plans (mla_set_plan_override)")
     ap.add_argument("--merge", default=None, choices=("kernel", "fused"),
                     help="force where split sequences are merged (mla_set_plan_override)")
@@ -858,6 +871,7 @@ def main():
     if args.decode_kernel or args.merge:
         import mla_paged_kv_02_amd as mla
         mla.set_plan_override(kernel=args.decode_kernel, merge=args.merge)
+        FORCED_KERNEL = args.decode_kernel
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
     if fp8:
         names = [n for n in names if WORKLOADS[n].h_q * WORKLOADS[n].s_q <= 64]

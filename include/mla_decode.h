@@ -234,14 +234,16 @@ mla_status mla_decode_fwd_noalloc(const void* q, const void* kv_cache, const int
  *   kernel  -1 the default choice, 0 always the 16-row organisation (each
  *           wave its own key stripe), 1 always the score/value-wave
  *           organisation (blocks of 16, 32 or 64 rows, the smallest that
- *           holds the rows)
+ *           holds the rows), 2 always the fused-wave organisation (blocks of
+ *           128 rows, each wave scoring and accumulating 32 of them)
  *   merge   -1 the default choice, 0 split sequences are merged by a combine
  *           kernel after decode, 1 by the last decode workgroup of each
+ *           (the fused-wave organisation always uses the combine kernel)
  *
  * The plan (metadata, size queries) and the decode call it serves must be
  * made under the same setting: a plan built under another kernel choice no
  * longer matches the call (see mla_check_metadata_host). Returns
- * MLA_ERR_INVALID_ARG for kernel or merge outside -1..1.
+ * MLA_ERR_INVALID_ARG for kernel outside -1..2 or merge outside -1..1.
  */
 mla_status mla_set_plan_override(int kernel, int merge);
 

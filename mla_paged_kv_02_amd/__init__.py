@@ -350,10 +350,10 @@ def mha_decode_fwd(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
 
 
 def set_plan_override(kernel: Optional[str] = None, merge: Optional[str] = None) -> None:
-    """Testing hook (mla_set_plan_override): kernel None | "rows16" | "ws",
-    merge None | "kernel" | "fused"; None restores the default choice. Build
-    plans after setting it."""
-    k = {None: -1, "rows16": 0, "ws": 1}[kernel]
+    """Testing hook (mla_set_plan_override): kernel None | "rows16" | "ws" |
+    "fw", merge None | "kernel" | "fused"; None restores the default choice.
+    Build plans after setting it."""
+    k = {None: -1, "rows16": 0, "ws": 1, "fw": 2}[kernel]
     m = {None: -1, "kernel": 0, "fused": 1}[merge]
     check(lib().mla_set_plan_override(k, m), "mla_set_plan_override")
 

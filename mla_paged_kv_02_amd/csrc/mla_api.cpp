@@ -106,16 +106,25 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // below 64 rows, 64-row blocks from 64 rows on (at exactly 64 the 16-row
     // kernel would stream every page four times, once per row block, and
     // its per-CU load rate then bounds it: on the long-context workload the
-    // 64-row kernel is 15% faster despite its larger partials). The FP8
-    // cache has only the 16-row kernel: its plans take it up to 64 rows.
+    // 64-row kernel is 15% faster despite its larger partials). 128-row
+    // blocks whose four waves each score and accumulate 32 rows (override 2)
+    // stream each page once per 128 rows, but one wave per SIMD keeps too few
+    // LDS reads in flight: at 128 heads they are 13-15% slower than two
+    // 64-row blocks. The FP8 cache has only the 16-row kernel: its plans take
+    // it up to 64 rows.
     if (fp8 && pl.M > 64) return false;
     DecodeKernel k = (pl.M < 64 || fp8) ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
     const int ov = g_kernel_override.load(std::memory_order_relaxed);
     if (ov == 0 && !fp8) k = DecodeKernel::Rows16;
     if (ov == 1 && !fp8) k = DecodeKernel::WaveSplit;
+    if (ov == 2 && !fp8) k = DecodeKernel::FusedWave;
     // the score/value-wave kernel's block: the smallest of 16, 32 and 64
     // rows that holds the sequence's rows, 64 beyond
-    const int tm = k == DecodeKernel::Rows16 ? 16 : pl.M <= 16 ? 16 : pl.M <= 32 ? 32 : 64;
+    const int tm = k == DecodeKernel::Rows16      ? 16
+                   : k == DecodeKernel::FusedWave ? 128
+                   : pl.M <= 16                   ? 16
+                   : pl.M <= 32                   ? 32
+                                                  : 64;
     pl.kernel = k;
     pl.tm = tm;
     pl.R = (pl.M + tm - 1) / tm;
@@ -148,6 +157,8 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.fused_combine = pl.P <= pl.batch && pl.M < 128;
     const int mo = g_merge_override.load(std::memory_order_relaxed);
     if (mo >= 0) pl.fused_combine = mo == 1;
+    // the 128-row kernel leaves every merge to the combine kernel
+    if (k == DecodeKernel::FusedWave) pl.fused_combine = false;
     *plan = pl;
     return true;
 }
@@ -435,7 +446,7 @@ mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t
 }
 
 mla_status mla_set_plan_override(int kernel, int merge) {
-    if (kernel < -1 || kernel > 1 || merge < -1 || merge > 1) return MLA_ERR_INVALID_ARG;
+    if (kernel < -1 || kernel > 2 || merge < -1 || merge > 1) return MLA_ERR_INVALID_ARG;
     g_kernel_override.store(kernel, std::memory_order_relaxed);
     g_merge_override.store(merge, std::memory_order_relaxed);
     return MLA_OK;

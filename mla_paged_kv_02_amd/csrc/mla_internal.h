@@ -12,9 +12,9 @@ namespace mla {
 // the grid is P*R workgroups.
 //   Rows16:    tm = 16, four waves each owning a key stripe of every page;
 //   WaveSplit: tm = 16, 32 or 64, score waves and four value waves;
+//   FusedWave: tm = 128, four waves each scoring and accumulating 32 rows;
 //   Rows16Fp8: the Rows16 organisation over the FP8 page format.
-// WaveSplit blocks hold 16, 32 or 64 rows (tm).
-enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8 };
+enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8, FusedWave };
 
 struct Plan {
     int batch, h_q, s_q, M;
@@ -67,6 +67,7 @@ hipError_t launch_split_metadata(const int32_t* seqlens, int batch, int num_part
 hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_fw(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 

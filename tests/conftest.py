@@ -9,7 +9,7 @@ if ROOT not in sys.path:
 
 
 def pytest_addoption(parser):
-    parser.addoption("--decode-kernel", default=None, choices=("rows16", "ws"),
+    parser.addoption("--decode-kernel", default=None, choices=("rows16", "ws", "fw"),
                      help="GPU tests: force every BF16 decode plan onto one kernel organisation "
                           "(mla_set_plan_override)")
 
@@ -31,12 +31,13 @@ def _plan_override(request):
 
 @pytest.fixture
 def plan_override(request):
-    """Setter for mla_set_plan_override inside a test (kept with --decode-kernel)."""
+    """Setter for mla_set_plan_override inside a test; the kernel defaults
+    to --decode-kernel's."""
     import mla_paged_kv_02_amd as mla
-    kernel = request.config.getoption("--decode-kernel")
+    default_kernel = request.config.getoption("--decode-kernel")
 
-    def set_(merge=None):
-        mla.set_plan_override(kernel=kernel, merge=merge)
+    def set_(merge=None, kernel=None):
+        mla.set_plan_override(kernel=kernel or default_kernel, merge=merge)
     return set_
 
 

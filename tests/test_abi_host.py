@@ -293,7 +293,7 @@ def test_plan_header_check_on_host_plans():
 
 def test_plan_override_is_checked_and_shapes_the_plan():
     lib = _lib.lib()
-    assert lib.mla_set_plan_override(2, -1) == INVALID
+    assert lib.mla_set_plan_override(3, -1) == INVALID
     assert lib.mla_set_plan_override(-1, -2) == INVALID
     lens = [300, 70, 129, 5000]
     try:
@@ -303,12 +303,27 @@ def test_plan_override_is_checked_and_shapes_the_plan():
         assert lib.mla_set_plan_override(0, -1) == OK          # 16-row blocks at 64 rows: R = 4
         r16_plan = _host_plan(lens, 64, 1, 64)
         assert r16_plan[8] == 4
+        assert lib.mla_set_plan_override(2, 1) == OK           # 128-row fused-wave blocks at 64 rows: R = 1
+        fw_plan = _host_plan(lens, 64, 1, 64)
+        assert fw_plan[8] == 1 and fw_plan[3] == 9
         # a plan built under one setting does not match a call under the default
         assert lib.mla_set_plan_override(-1, -1) == OK
         assert _check_meta(ws_plan, 4, 32, 1, 64) == INVALID
         assert _check_meta(r16_plan, 4, 64, 1, 64) == INVALID
+        assert _check_meta(fw_plan, 4, 64, 1, 64) == INVALID
     finally:
         lib.mla_set_plan_override(-1, -1)
+
+
+def test_default_plan_row_blocks():
+    """Row blocks of the default plans: 16 rows below 64 rows per sequence,
+    64 from there (header word 8 is R, word 3 the per-segment cost
+    1 + rows/16)."""
+    lens = [300, 70, 129, 5000]
+    for h_q, s_q, r, cseg in [(16, 1, 1, 2), (32, 1, 2, 2), (64, 1, 1, 5), (64, 2, 2, 5), (128, 1, 2, 5),
+                              (128, 2, 4, 5), (128, 8, 16, 5)]:
+        plan = _host_plan(lens, h_q, s_q, 64)
+        assert (plan[8], plan[3]) == (r, cseg), (h_q, s_q, plan[:9])
 
 
 def _noalloc(**kw):

@@ -58,6 +58,17 @@ def test_small_shapes(case):
     _check(inp, tag=f"small[{case}]")
 
 
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_small_shapes_fused_wave_forced(case, plan_override):
+    """Every small case on the 128-row fused-wave organisation: rows past M
+    inside its block (down to 8 of 128 in use), ragged tails, empty
+    sequences, causal masks, several row blocks per sequence."""
+    plan_override(kernel="fw")
+    seqlens, s_q, h_q, causal = SMALL_CASES[case]
+    inp = make_inputs(seqlens, s_q, h_q, seed=100 + case, causal=causal)
+    _check(inp, tag=f"small-fw[{case}]")
+
+
 @pytest.mark.parametrize("parts", [1, 8, 24, 64, 512])
 @pytest.mark.parametrize("shape", [(16, 1, False), (64, 1, False), (128, 2, True)])
 def test_forced_splits(parts, shape):
@@ -252,6 +263,17 @@ def test_reference_restart_on_dominant_key(h_q, s_q, causal, parts):
     inp = make_inputs([3000, 700, 150], s_q, h_q, seed=41 + parts, causal=causal)
     inp = _with_dominant_keys(inp, [(0, 2500), (1, 600), (2, 100)])
     out, lse = _check(inp, num_partitions=parts, tag=f"restart h_q={h_q} parts={parts}")
+    assert np.all(np.isfinite(lse))
+
+
+@pytest.mark.parametrize("h_q,s_q,causal,parts", [(16, 1, False, 0), (16, 1, False, 16), (64, 1, False, 24)])
+def test_reference_restart_fused_wave_forced(h_q, s_q, causal, parts, plan_override):
+    """The redo of a segment on the fused-wave organisation when a later key
+    dominates, with fewer rows than its block and with splits."""
+    plan_override(kernel="fw")
+    inp = make_inputs([3000, 700, 150], s_q, h_q, seed=43 + parts, causal=causal)
+    inp = _with_dominant_keys(inp, [(0, 2500), (1, 600), (2, 100)])
+    out, lse = _check(inp, num_partitions=parts, tag=f"restart-fw h_q={h_q} parts={parts}")
     assert np.all(np.isfinite(lse))
 
 
