@@ -353,11 +353,10 @@ FORCED_KERNEL = None
 def decode_kernel_name(fp8: bool, rows: int) -> str:
     """The decode kernel a plan of `rows` query rows per sequence runs: the
     library picks 16-row blocks below 64 rows and 64-row score/value blocks
-    from there (--decode-kernel forces one); the FP8 cache has the 16-row
-    kernel only."""
-    if fp8:
-        return "mla_decode_rows16_fp8_kernel"
+    from there, over either cache (--decode-kernel forces one)."""
     kind = FORCED_KERNEL or ("rows16" if rows < 64 else "ws")
+    if fp8:
+        return "mla_decode_rows16_fp8_kernel" if kind == "rows16" else "mla_decode_ws_kernel<4, true>"
     return {"rows16": "mla_decode_rows16_kernel", "ws": "mla_decode_ws_kernel",
             "fw": "mla_decode_fw_kernel"}[kind]
 
@@ -873,8 +872,6 @@ def main():
         mla.set_plan_override(kernel=args.decode_kernel, merge=args.merge)
         FORCED_KERNEL = args.decode_kernel
     names = list(WORKLOADS) if args.workload == "all" else [args.workload]
-    if fp8:
-        names = [n for n in names if WORKLOADS[n].h_q * WORKLOADS[n].s_q <= 64]
     ctx = None if args.no_stream_context else streaming_context()
     rotate = int(args.rotate_gib * (1 << 30))
     for name in names:
@@ -890,7 +887,7 @@ def main():
             import torch
             others = {}
             for other in WORKLOADS:
-                if other == name or (fp8 and WORKLOADS[other].h_q * WORKLOADS[other].s_q > 64):
+                if other == name:
                     continue
                 torch.cuda.empty_cache()
                 others[other] = workload_summary(run_workload(other, args.steps, args.warmup, 0, rotate,

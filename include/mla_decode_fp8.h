@@ -45,9 +45,10 @@ extern "C" {
  * mla_get_split_metadata_fp8 - the split plan for mla_decode_fwd_fp8.
  *
  * Same arguments, layout and semantics as mla_get_split_metadata. The FP8
- * decode uses the 16-row kernels up to 64 rows, where the BF16 decode of a
- * 64-row query block uses the 64-row kernel, so the two calls' plans differ
- * there; mla_metadata_bytes and mla_workspace_bytes cover both.
+ * decode uses 16-row blocks below 64 rows and 64-row blocks from 64 rows
+ * on, like the BF16 decode, but never 16- or 32-row score/value blocks, so
+ * the two calls' plans can differ; mla_metadata_bytes and
+ * mla_workspace_bytes cover both.
  */
 mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q, int s_q,
                                       int num_partitions, int32_t* metadata, size_t metadata_bytes,
@@ -61,10 +62,13 @@ mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q
  *   metadata   from mla_get_split_metadata_fp8 (or NULL: computed in-call)
  *   (all other arguments as for mla_decode_fwd)
  *
- * Supported: h_q * s_q <= 64 (the 16-row kernels); larger query blocks
- * return MLA_ERR_UNSUPPORTED, as does a process whose kernel choice was
- * forced to the 64-row kernel. Latent bytes of used tokens must not be NaN
- * patterns; scales must be finite.
+ * Supported: h_q * s_q up to MLA_MAX_ROWS, as for mla_decode_fwd. Below 64
+ * rows a 16-row kernel converts each wave's key stripe; from 64 rows a
+ * 64-row kernel converts each half page once per workgroup into the BF16
+ * layout its products read. A process whose kernel choice was forced to the
+ * 16-row organisation (mla_set_plan_override) gets MLA_ERR_UNSUPPORTED above
+ * 64 rows; the fused-wave override does not apply to FP8. Latent bytes of
+ * used tokens must not be NaN patterns; scales must be finite.
  */
 mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t* block_table,
                               int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q, int h_q,

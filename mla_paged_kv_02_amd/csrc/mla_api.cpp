@@ -110,21 +110,33 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // blocks whose four waves each score and accumulate 32 rows (override 2)
     // stream each page once per 128 rows, but one wave per SIMD keeps too few
     // LDS reads in flight: at 128 heads they are 13-15% slower than two
-    // 64-row blocks. The FP8 cache has only the 16-row kernel: its plans take
-    // it up to 64 rows.
-    if (fp8 && pl.M > 64) return false;
-    DecodeKernel k = (pl.M < 64 || fp8) ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
+    // 64-row blocks. The FP8 cache has the same split: 16-row blocks below 64
+    // rows, 64-row score/value blocks (with the FP8 fill) from 64 rows on.
     const int ov = g_kernel_override.load(std::memory_order_relaxed);
-    if (ov == 0 && !fp8) k = DecodeKernel::Rows16;
-    if (ov == 1 && !fp8) k = DecodeKernel::WaveSplit;
-    if (ov == 2 && !fp8) k = DecodeKernel::FusedWave;
+    DecodeKernel k;
+    if (fp8) {
+        k = pl.M < 64 ? DecodeKernel::Rows16Fp8 : DecodeKernel::WaveSplitFp8;
+        if (ov == 0) {
+            if (pl.M > 64) return false;   // the 16-row FP8 kernel stops at four row blocks
+            k = DecodeKernel::Rows16Fp8;
+        }
+        if (ov == 1) k = DecodeKernel::WaveSplitFp8;
+    } else {
+        k = pl.M < 64 ? DecodeKernel::Rows16 : DecodeKernel::WaveSplit;
+        if (ov == 0) k = DecodeKernel::Rows16;
+        if (ov == 1) k = DecodeKernel::WaveSplit;
+        if (ov == 2) k = DecodeKernel::FusedWave;
+    }
     // the score/value-wave kernel's block: the smallest of 16, 32 and 64
-    // rows that holds the sequence's rows, 64 beyond
-    const int tm = k == DecodeKernel::Rows16      ? 16
-                   : k == DecodeKernel::FusedWave ? 128
-                   : pl.M <= 16                   ? 16
-                   : pl.M <= 32                   ? 32
-                                                  : 64;
+    // rows that holds the sequence's rows, 64 beyond (64 always over FP8)
+    const bool rows16 = k == DecodeKernel::Rows16 || k == DecodeKernel::Rows16Fp8;
+    const bool ws = k == DecodeKernel::WaveSplit || k == DecodeKernel::WaveSplitFp8;
+    const int tm = rows16                           ? 16
+                   : k == DecodeKernel::FusedWave    ? 128
+                   : k == DecodeKernel::WaveSplitFp8 ? 64
+                   : pl.M <= 16                      ? 16
+                   : pl.M <= 32                      ? 32
+                                                     : 64;
     pl.kernel = k;
     pl.tm = tm;
     pl.R = (pl.M + tm - 1) / tm;
@@ -137,7 +149,7 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
         // more than its share), and a quarter fewer 128 KB FP32 partials
         // shortens the combine (4 sequences of 1K-64K tokens at 64 heads:
         // call 53.4 vs 55.5 us, decode kernel unchanged).
-        if (k == DecodeKernel::WaveSplit && tm == 64 && pl.R == 1) p = cus * 3 / 4;
+        if (ws && tm == 64 && pl.R == 1) p = cus * 3 / 4;
         if (p < 1) p = 1;
     }
     pl.P = (p + 7) / 8 * 8;  // whole groups of 8 for the XCD-aware block mapping
@@ -358,10 +370,8 @@ mla_status decode_fwd_impl(const void* q, const void* kv_cache, const int32_t* b
     if (!make_plan(batch, h_q, s_q, num_partitions,
                    num_partitions > 0 ? 0 : current_cu_count(), &pl, fp8))
         return MLA_ERR_UNSUPPORTED;
-    if (fp8) {
-        if (pl.kernel != DecodeKernel::Rows16) return MLA_ERR_UNSUPPORTED;
-        pl.kernel = DecodeKernel::Rows16Fp8;
-    }
+    if (fp8 != (pl.kernel == DecodeKernel::Rows16Fp8 || pl.kernel == DecodeKernel::WaveSplitFp8))
+        return MLA_ERR_UNSUPPORTED;
     const WorkspaceLayout wl = workspace_layout(pl, metadata == nullptr);
     if (noalloc) {
         if (wl.total > (size_t)MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_SCRATCH_LIMIT;

@@ -9,6 +9,7 @@ hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t s
         case DecodeKernel::WaveSplit: return launch_decode_ws(plan, args, stream);
         case DecodeKernel::Rows16Fp8: return launch_decode_rows16_fp8(plan, args, stream);
         case DecodeKernel::FusedWave: return launch_decode_fw(plan, args, stream);
+        case DecodeKernel::WaveSplitFp8: return launch_decode_ws_fp8(plan, args, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -42,6 +42,26 @@
 // wait for them is explicit. The two roles are separate code paths with the
 // same barrier sequence, so the score waves' query registers and the value
 // waves' accumulators share the register file and two waves fit per SIMD.
+//
+// FP8 latent cache (64-row blocks; page layout of mla_decode_fp8.h: four
+// 16-token groups, each its E4M3 latent rows, BF16 rotary rows and FP32
+// per-token scales; latent coordinate d of token t is e4m3 * scale[t]). The
+// ring keeps exactly the BF16 slot layout above, so both products read it
+// unchanged; what differs is how a slot is filled and where the scale goes:
+//
+//  * value wave v loads rows 8v..8v+7 of a half page (latent bytes, rotary
+//    row, scale) into registers at the end of the step two before the one
+//    that scores it, and at the end of the step before, converts the latent
+//    bytes to BF16 (exact: every E4M3 value is a BF16 value), writes them,
+//    the rotary part and the scale into the half page's slot and loads the
+//    next half page into the same registers; each half page is converted
+//    once per workgroup;
+//  * the score waves keep the latent and rotary parts of a score apart
+//    (latent k-steps, then the two rotary k-steps) and combine them as
+//    scale * latent + rotary; the value product sees p_t * scale_t, the
+//    normaliser sums p_t.
+// These loads are ordinary ones, tracked and waited for by the compiler; the
+// kernel issues no untracked load in this mode.
 #include "mla_common.h"
 #include "mla_fused_combine.h"
 #include "mla_internal.h"
@@ -73,6 +93,43 @@ constexpr int kVTiles = 8;                      // value tiles (16 columns) per 
 constexpr float kRefMargin = 32.f;
 constexpr float kHeadroom = 64.f;
 
+// FP8 page: four groups of 16 tokens, each 16 E4M3 latent rows (512 B), 16
+// BF16 rotary rows (128 B) and 16 FP32 scales
+constexpr int kF8Group = 16 * 512 + 16 * 128 + 16 * 4;   // 10304
+constexpr int kF8PageBytes = 4 * kF8Group;                 // 41216
+constexpr int kF8RopeOff = 16 * 512;
+constexpr int kF8ScaleOff = 16 * 512 + 16 * 128;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// A value-wave lane's share of one half page of the FP8 cache: 64 latent
+// bytes (row 8v + lane/8, bytes 64 (lane % 8) ..), 16 rotary bytes of the
+// same row (bytes 16 (lane % 8) ..) and the row's scale.
+struct F8Part {
+    u32x4 lat[4];
+    u32x4 rope;
+    float sc;
+};
+
+// 16 E4M3 values -> 16 BF16 values, exact (every E4M3 value is a BF16 value)
+__device__ __forceinline__ void e4m3x16_to_bf16_ws(const u32x4& w, bf16x8& lo, bf16x8& hi) {
+    bf16x2 p[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
+        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lo[2 * i] = p[i][0];
+        lo[2 * i + 1] = p[i][1];
+        hi[2 * i] = p[4 + i][0];
+        hi[2 * i + 1] = p[4 + i][1];
+    }
+}
+
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 // a slot's loads are followed by one more slot's loads before it is read
 constexpr int kWaitSlot = wait_vm_lgkm0(kWLoads);
@@ -96,9 +153,12 @@ __device__ __forceinline__ void block_barrier() {
 
 }  // namespace
 
-template <int kRT>
+template <int kRT, bool kFp8>
 __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(DecodeArgs a) {
     using Sh = WsShape<kRT>;
+    // the FP8 fill spreads a half page over eight waves: 64-row blocks only
+    static_assert(!kFp8 || kRT == 4, "FP8 cache: 64-row blocks");
+    constexpr int kPB = kFp8 ? kF8PageBytes : kPageBytes;
     constexpr int kRows = Sh::kRows;
     constexpr int kSW = Sh::kScoreWaves;
     constexpr int kPBytes = kRT * 1024;
@@ -115,6 +175,8 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     // by every wave after the next barrier
     __shared__ int restart_flag[2];
     __shared__ int last_flag;   // this workgroup merges a split sequence
+    // FP8: the per-token scales of the half page in each ring slot
+    __shared__ __attribute__((aligned(16))) float slot_scale[kFp8 ? 4 : 1][kCRows];
 
     if (!plan_matches_or_poison<Sh::kThreads>(a)) return;
     const int lane = threadIdx.x & 63;
@@ -180,7 +242,7 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     int fc = 0;
     auto fpage_of = [&]() {
         const int32_t* bt_row = a.block_table + (size_t)fseg.b * a.max_blocks;
-        return reinterpret_cast<const uint8_t*>(a.kv) + (size_t)ld_const_ws(bt_row, fseg.lo + fc / 2) * kPageBytes;
+        return reinterpret_cast<const uint8_t*>(a.kv) + (size_t)ld_const_ws(bt_row, fseg.lo + fc / 2) * kPB;
     };
     const uint8_t* fpage = nullptr;
     // the half page taken for issue: its page, which half, and the rows of
@@ -211,6 +273,37 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     auto issue_all = [&](uint32_t dst) {
 #pragma unroll
         for (int j = 0; j < kWLoads; ++j) issue_one(dst, j);
+    };
+
+    // ---- FP8 (value waves): rows 8 sw .. 8 sw + 7 of the taken half page
+    // into registers, and from registers into a ring slot. Rows at or past
+    // the sequence end read row 0 of the page (a written token: finite).
+    const int f8_hr = 8 * sw + (lane >> 3);   // the lane's row of the half page
+    auto f8_load = [&](F8Part& fp) {
+        const int prow = t_half * kCRows + f8_hr;
+        const int srow = prow < t_rows ? prow : 0;
+        const uint8_t* gb = t_src + (srow >> 4) * kF8Group;
+        const int i = srow & 15;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            fp.lat[k] = *reinterpret_cast<const u32x4*>(gb + i * 512 + (lane & 7) * 64 + 16 * k);
+        fp.rope = *reinterpret_cast<const u32x4*>(gb + kF8RopeOff + i * 128 + (lane & 7) * 16);
+        fp.sc = *reinterpret_cast<const float*>(gb + kF8ScaleOff + i * 4);
+    };
+    auto f8_store = [&](const F8Part& fp, int slot) {
+        uint8_t* row = ring + slot * kCBytes + f8_hr * kRowBytes;
+        const int swz = lds_swizzle(f8_hr);
+        const int c0 = 8 * (lane & 7);   // the lane's first latent chunk (8 BF16 each)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bf16x8 lo, hi;
+            e4m3x16_to_bf16_ws(fp.lat[k], lo, hi);
+            *reinterpret_cast<bf16x8*>(row + (((c0 + 2 * k) ^ swz) << 4)) = lo;
+            *reinterpret_cast<bf16x8*>(row + (((c0 + 2 * k + 1) ^ swz) << 4)) = hi;
+        }
+        const int rc = kHeadDimV / 8 + (lane & 7);   // rotary chunk 64..71
+        *reinterpret_cast<u32x4*>(row + ((rc ^ swz) << 4)) = fp.rope;
+        if ((lane & 7) == 0) slot_scale[kFp8 ? slot : 0][f8_hr] = fp.sc;
     };
 
     // per-lane LDS offsets inside a slot: K fragment of k-step ks for key row
@@ -248,7 +341,23 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
 
         // value waves: the stream's first two half pages
         bool issued_next = false;   // the half page after the one waited for is in flight
-        if constexpr (!kScorer) {
+        // FP8: the stream's next half page not yet in the ring, in registers
+        F8Part f8;
+        bool f8_got = false;
+        // FP8 (value waves): write the stream's next half page into slot
+        // `slot` and load the one after it
+        auto f8_prime = [&](int slot) {
+            if (take()) {
+                f8_load(f8);
+                f8_store(f8, slot);
+            }
+            f8_got = take();
+            if (f8_got) f8_load(f8);
+        };
+        if constexpr (kFp8 && !kScorer) {
+            if (fseg.b >= 0) fpage = fpage_of();
+            f8_prime(0);
+        } else if constexpr (!kScorer) {
             if (fseg.b >= 0) fpage = fpage_of();
             if (take()) issue_all(ring_lds);
             issued_next = take();
@@ -314,7 +423,7 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                 auto step = [&](auto sc) -> bool {
                     constexpr int S = decltype(sc)::value;
                     const uint8_t* slot_cur = ring + ((S + soff) & 3) * kCBytes;
-                    if constexpr (!kScorer) {
+                    if constexpr (!kScorer && !kFp8) {
                         // my part of half page c (at most the next one's loads are younger)
                         if (c < nch) {
                             if (issued_next) wait_then_fence<kWaitSlot>();
@@ -326,10 +435,14 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                     bool issue_now = false;
                     uint32_t dst = 0;
                     if constexpr (!kScorer) {
-                        issue_now = c < nch && take();
-                        dst = ring_lds + ((S + soff + 2) & 3) * kCBytes;
-                        if (c == 0 && issue_now) issue_all(dst);
+                        if constexpr (!kFp8) {
+                            issue_now = c < nch && take();
+                            dst = ring_lds + ((S + soff + 2) & 3) * kCBytes;
+                            if (c == 0 && issue_now) issue_all(dst);
+                        }
                     } else if (c < nch) {
+                        // FP8: the per-token scales of this wave's keys (folded into P)
+                        f32x4 my_scale = {1.f, 1.f, 1.f, 1.f};
                         // ---- S^T = K Q^T for key tile `tile` of half page c,
                         // every row tile of this wave; one K fragment feeds them
                         // all. Lane holds keys key0 + j (j < 4) of rows lrow[r],
@@ -337,6 +450,7 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                         auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&lm)[NR]) {
                             const uint8_t* kb = slot_cur + tile * 16 * kRowBytes;
                             f32x4 sp[NR][2];
+                            f32x4 slat[NR];   // FP8: the latent part, scaled below
 #pragma unroll
                             for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -348,23 +462,38 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                             for (int d = 0; d < KD; ++d) kf[d] = lds_read16(kb + k_off(d));
 #pragma unroll
                             for (int ks = 0; ks < kKS; ++ks) {
+                                if (kFp8 && ks == kHeadDimV / 32) {
+                                    // latent k-steps done: keep them, accumulate the rotary part apart
+#pragma unroll
+                                    for (int r = 0; r < NR; ++r) {
+                                        slat[r] = sp[r][0] + sp[r][1];
+                                        sp[r][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                                        sp[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                                    }
+                                }
 #pragma unroll
                                 for (int r = 0; r < NR; ++r) sp[r][ks & 1] = mfma16(kf[ks % KD], qf[r][ks], sp[r][ks & 1]);
                                 if (ks + KD < kKS) kf[ks % KD] = lds_read16(kb + k_off(ks + KD));
                                 __builtin_amdgcn_sched_barrier(0);
                             }
                             const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + tile * 16 + 4 * g;
+                            f32x4 sck = {0.f, 0.f, 0.f, 0.f};
+                            if constexpr (kFp8)
+                                sck = *reinterpret_cast<const f32x4*>(&slot_scale[kFp8 ? (S + soff) & 3 : 0][tile * 16 + 4 * g]);
 #pragma unroll
                             for (int r = 0; r < NR; ++r) {
                                 float m = -INFINITY;
 #pragma unroll
                                 for (int j = 0; j < 4; ++j) {
-                                    const float v = (key0 + j < L[r]) ? sp[r][0][j] + sp[r][1][j] : -INFINITY;
+                                    const float raw = kFp8 ? fmaf(slat[r][j], sck[j], sp[r][0][j] + sp[r][1][j])
+                                                           : sp[r][0][j] + sp[r][1][j];
+                                    const float v = (key0 + j < L[r]) ? raw : -INFINITY;
                                     sv[r][j] = v;
                                     m = fmaxf(m, v);
                                 }
                                 lm[r] = m;
                             }
+                            if (kFp8 && tile == kt) my_scale = sck;
                         };
                         // row maximum in the log2 domain (scale > 0: the
                         // maximum commutes with it)
@@ -414,7 +543,9 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                                     pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r][j], a.scale_log2, neg_m));
                                     l_run[r] += pw[j];
                                 }
-                                // B = P^T of row tile rt0 + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j
+                                // B = P^T of row tile rt0 + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j;
+                                // FP8: the value product sees p_t * scale_t, the sum p_t alone
+                                if constexpr (kFp8) pw *= my_scale;
                                 *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(rt0 + r) * 1024 + lane * 16 + kt * 8]) =
                                     pack_bf16x4(pw);
                             }
@@ -428,7 +559,7 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                         bf16x8 pf[kRT];
 #pragma unroll
                         for (int rt = 0; rt < kRT; ++rt) pf[rt] = lds_read16(pb + rt * 1024);
-                        constexpr int VD = 5;
+                        constexpr int VD = kFp8 ? 3 : 5;
                         auto v_frag = [&](int t) {
                             const int dt = sw * kVTiles + t;
                             const int off = vofs[dt & 3] + (dt >> 2) * 128;
@@ -450,6 +581,17 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                     }
                     if constexpr (!kScorer) {
                         if (c < nch) issued_next = issue_now;
+                    }
+                    if constexpr (kFp8 && !kScorer) {
+                        // the stream's next half page (loaded at the end of
+                        // the step before) into its slot, which the value
+                        // waves left two steps ago (the next barrier publishes
+                        // it), then the one after it into the registers
+                        if (c < nch) {
+                            if (f8_got) f8_store(f8, (S + soff + 1) & 3);
+                            f8_got = take();
+                            if (f8_got) f8_load(f8);
+                        }
                     }
                     ++c;
                     return c <= nch;
@@ -487,7 +629,15 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                     if constexpr (kScorer) {
 #pragma unroll
                         for (int r = 0; r < NR; ++r) m_ref[r] = row_m[lrow[r]];
-                    } else {
+                    }
+                    if constexpr (kFp8 && !kScorer) {
+                        // restart the stream at this segment's start and
+                        // write its first half page again
+                        fseg = seg;
+                        fc = 0;
+                        fpage = fpage_of();
+                        f8_prime(soff);
+                    } else if constexpr (!kScorer) {
                         // drain the ring and refill it from this segment's start
                         wait_then_fence<kWaitAll>();
                         fseg = seg;
@@ -564,10 +714,10 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     else run(std::false_type{});
 }
 
-template <int kRT>
+template <int kRT, bool kFp8 = false>
 static hipError_t launch_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
-    hipLaunchKernelGGL(mla_decode_ws_kernel<kRT>, dim3(plan.P * plan.R), dim3(WsShape<kRT>::kThreads), 0, stream,
-                       args);
+    hipLaunchKernelGGL((mla_decode_ws_kernel<kRT, kFp8>), dim3(plan.P * plan.R), dim3(WsShape<kRT>::kThreads), 0,
+                       stream, args);
     return hipGetLastError();
 }
 
@@ -578,6 +728,11 @@ hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_
         case 64: return launch_ws<4>(plan, args, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_ws_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
+    if (plan.tm != 64) return hipErrorInvalidValue;
+    return launch_ws<4, true>(plan, args, stream);
 }
 
 }  // namespace mla

@@ -13,8 +13,9 @@ namespace mla {
 //   Rows16:    tm = 16, four waves each owning a key stripe of every page;
 //   WaveSplit: tm = 16, 32 or 64, score waves and four value waves;
 //   FusedWave: tm = 128, four waves each scoring and accumulating 32 rows;
-//   Rows16Fp8: the Rows16 organisation over the FP8 page format.
-enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8, FusedWave };
+//   Rows16Fp8: the Rows16 organisation over the FP8 page format;
+//   WaveSplitFp8: the WaveSplit organisation (tm = 64) over the FP8 pages.
+enum class DecodeKernel { Rows16, WaveSplit, Rows16Fp8, FusedWave, WaveSplitFp8 };
 
 struct Plan {
     int batch, h_q, s_q, M;
@@ -68,6 +69,7 @@ hipError_t launch_decode(const Plan& plan, const DecodeArgs& args, hipStream_t s
 hipError_t launch_decode_rows16(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_fw(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
+hipError_t launch_decode_ws_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_decode_rows16_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const DecodeArgs& args, hipStream_t stream);
 

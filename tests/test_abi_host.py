@@ -191,7 +191,7 @@ def _decode_fp8(**kw):
     (dict(kv=None), INVALID), (dict(q=None), INVALID), (dict(batch=0), INVALID), (dict(causal=3), INVALID),
     (dict(scale=-1.0), INVALID), (dict(scale=-0.0), INVALID), (dict(scale=0.0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
-    (dict(h_q=128), UNSUPPORTED), (dict(h_q=16, s_q=8), UNSUPPORTED),
+    (dict(h_q=128, s_q=16), UNSUPPORTED),
     (dict(kv=FAKE + 4), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED), (dict(ws_bytes=1024), TOO_SMALL),
 ])
 def test_decode_fp8_argument_checks(kw, status):
@@ -215,19 +215,29 @@ def test_append_fp8_argument_checks(kw, status):
 def test_fp8_metadata_argument_checks():
     lib = _lib.lib()
     assert lib.mla_get_split_metadata_fp8(None, 2, 16, 1, 64, FAKE, 1 << 20, None) == INVALID
-    assert lib.mla_get_split_metadata_fp8(FAKE, 2, 128, 1, 64, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.mla_get_split_metadata_fp8(FAKE, 2, 128, 16, 64, FAKE, 1 << 20, None) == UNSUPPORTED
     assert lib.mla_get_split_metadata_fp8(FAKE, 2, 16, 1, 64, FAKE, 16, None) == TOO_SMALL
 
 
 def test_size_queries_cover_the_fp8_plan():
-    # at 64 rows the BF16 plan uses the 64-row kernel, the FP8 plan the
-    # 16-row one; one buffer must fit either, also for large batches
+    # the FP8 plan of 128 and 256 rows (64-row blocks: R = 2 and 4); one
+    # buffer must fit it, also for large batches
     lib = _lib.lib()
     for batch in (1, 64, 4096):
-        m = lib.mla_metadata_bytes(batch, 64, 1, 64)
-        w = lib.mla_workspace_bytes(batch, 64, 1, 64)
-        meta16 = 4 * (16 + 8 * 64 + 4 * batch + 4 * batch)      # P = 64, R = 4
-        assert m >= meta16 and w > 0
+        for s_q, r in ((1, 2), (2, 4)):
+            m = lib.mla_metadata_bytes(batch, 128, s_q, 64)
+            w = lib.mla_workspace_bytes(batch, 128, s_q, 64)
+            meta = 4 * (16 + 8 * 64 + 4 * batch + r * batch)      # P = 64
+            assert m >= meta and w > 0
+    # under the score/value override the BF16 plan of 32 rows uses 32-row
+    # blocks (per-segment cost 3), the FP8 one 64-row blocks (cost 5)
+    try:
+        assert lib.mla_set_plan_override(1, -1) == OK
+        lens = [300, 70, 129, 5000]
+        assert _host_plan(lens, 32, 1, 64)[3] == 3
+        assert _check_meta(_host_plan(lens, 32, 1, 64), 4, 32, 1, 64, fp8=1) == INVALID
+    finally:
+        lib.mla_set_plan_override(-1, -1)
 
 
 def _mha(**kw):
@@ -282,9 +292,10 @@ def test_plan_header_check_on_host_plans():
         bad[0] ^= 1
         assert _check_meta(bad, 4, h_q, s_q, parts) == INVALID           # not a plan
         assert _check_meta(meta, 4, h_q, s_q, parts, nbytes=60) == TOO_SMALL
-    # 64 rows: the BF16 call uses 64-row blocks (R = 1), the FP8 call 16-row
-    # blocks (R = 4); 16 rows: both use 16-row blocks and share the plan
-    assert _check_meta(_host_plan(lens, 64, 1, 64), 4, 64, 1, 64, fp8=1) == INVALID
+    # by default the BF16 and FP8 calls cut rows alike (16-row blocks below 64
+    # rows, 64-row blocks from there) and share the plan
+    assert _check_meta(_host_plan(lens, 64, 1, 64), 4, 64, 1, 64, fp8=1) == OK
+    assert _check_meta(_host_plan(lens, 128, 2, 64), 4, 128, 2, 64, fp8=1) == OK
     assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 16, 1, 64, fp8=1) == OK
     assert _lib.lib().mla_check_metadata_host(None, 1024, 4, 16, 1, 64, 0) == INVALID
     assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 16, 1, 64, fp8=2) == INVALID

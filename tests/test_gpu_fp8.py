@@ -52,6 +52,12 @@ FP8_CASES = [
     ([90, 45], 1, 24, False),
     ([150], 3, 8, True),
     ([40, 3, 129], 4, 16, True),
+    # 64-row blocks with the FP8 fill: one, two, several per sequence
+    ([1, 64, 65, 700], 1, 64, False),
+    ([200, 333], 1, 128, False),
+    ([2, 3, 65, 190], 2, 128, True),
+    ([150, 3, 1000, 64, 0], 8, 128, True),
+    ([300, 2, 77], 16, 64, False),
 ]
 
 
@@ -64,17 +70,18 @@ def test_fp8_small_shapes(case):
 
 
 @pytest.mark.parametrize("parts", [1, 8, 64, 512])
-@pytest.mark.parametrize("h_q", [16, 64])
+@pytest.mark.parametrize("h_q", [16, 64, 128])
 def test_fp8_forced_splits(parts, h_q):
     inp = make_inputs([900, 3, 2049, 64, 1500], 1, h_q, seed=310 + parts)
     codes, rope, scales = make_fp8_cache(inp, seed=410 + parts)
     _check(inp, codes, rope, scales, f"splits h_q={h_q}", num_partitions=parts)
 
 
-def test_fp8_poisoned_tails_are_ignored():
+@pytest.mark.parametrize("h_q", [16, 64])
+def test_fp8_poisoned_tails_are_ignored(h_q):
     """Unused rows of last pages hold NaN latent bytes, NaN rotary values and
     NaN scales: the output must be bitwise what clean tails give."""
-    inp = make_inputs([70, 5, 129, 64], 2, 16, seed=320, causal=True)
+    inp = make_inputs([70, 5, 129, 64], 2, h_q, seed=320, causal=True)
     codes, rope, scales = make_fp8_cache(inp, seed=420)
     out0, lse0 = _check(inp, codes, rope, scales, "clean tails")
     pc, pr, ps = codes.copy(), rope.copy(), scales.copy()
@@ -89,45 +96,53 @@ def test_fp8_poisoned_tails_are_ignored():
     assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
 
 
+@pytest.mark.parametrize("h_q", [16, 64])
 @pytest.mark.parametrize("mode", ["fused", "kernel"])
-def test_fp8_combine_modes(mode, plan_override):
+def test_fp8_combine_modes(mode, h_q, plan_override):
     plan_override(merge=mode)
-    inp = make_inputs([0, 900, 3, 2049, 64, 1500, 0, 777], 1, 16, seed=330)
+    inp = make_inputs([0, 900, 3, 2049, 64, 1500, 0, 777], 1, h_q, seed=330)
     codes, rope, scales = make_fp8_cache(inp, seed=430)
     for parts in (8, 64):
         _check(inp, codes, rope, scales, f"combine {mode}", num_partitions=parts)
 
 
-def test_fp8_reference_restart_on_dominant_key():
+@pytest.mark.parametrize("h_q,s_q", [(16, 1), (64, 1), (128, 2)])
+def test_fp8_reference_restart_on_dominant_key(h_q, s_q):
     """Queries of 1.0 and, late in each sequence, a token whose latent values
-    are all 448 * (8/448) = 8 and whose rotary values are 8: its score is
-    ~2.8e2 in log2 units against ~1e1 for the others, far above the first
-    maximum plus the headroom, so the kernel must raise the reference and
-    restart the segment; the output is then ~8 and must match the oracle."""
+    are all 448 * (0.5/448) = 0.5 and whose rotary values are 32: its score
+    (512 * 0.5 + 64 * 32 = 2304 before the 1/24 scale, ~1.4e2 in log2 units)
+    is far above the others (~1e1) and the first maximum plus the headroom,
+    so the kernel must raise the reference and restart the segment. The
+    output is then ~0.5, inside the range the absolute output gate is stated
+    for (a BF16 output of magnitude 8 alone may round by 0.031), and must
+    match the oracle."""
     import dataclasses
-    inp = make_inputs([3000, 700, 150], 1, 16, seed=340)
+    inp = make_inputs([3000, 700, 150], s_q, h_q, seed=340)
     inp = dataclasses.replace(inp, q_bits=np.full_like(inp.q_bits, 0x3F80))
     codes, rope, scales = make_fp8_cache(inp, seed=440)
     for b, t in ((0, 2900), (1, 650), (2, 100)):
         phys, r = inp.block_table[b, t // 64], t % 64
         codes[phys, r] = 0x7E
-        scales[phys, r] = np.float32(8.0 / 448.0)
-        rope[phys, r] = 0x4100
+        scales[phys, r] = np.float32(0.5 / 448.0)
+        rope[phys, r] = 0x4200
     for parts in (0, 16):
         out, lse = _check(inp, codes, rope, scales, f"dominant key parts={parts}", num_partitions=parts)
         assert np.all(np.isfinite(lse))
 
 
-@pytest.mark.parametrize("name", ["memory_bound", "long_context"])
+@pytest.mark.parametrize("name", ["memory_bound", "long_context", "compute_leaning", "multi_token"])
 def test_fp8_workload_full_size(name):
     inp = make_workload_inputs(name)
     codes, rope, scales = make_fp8_cache(inp, seed=450)
     _check(inp, codes, rope, scales, name, seqs=list(range(inp.batch)))
 
 
-def test_fp8_rejects_large_query_blocks():
+def test_fp8_rejects_large_query_blocks_on_the_16_row_organisation(plan_override):
+    """Forced onto the 16-row FP8 kernel, a 128-row query block is
+    refused (that kernel stops at four row blocks)."""
     import torch
     import mla_paged_kv_02_amd as mla
+    plan_override(kernel="rows16")
     inp = make_inputs([100], 1, 128, seed=350)
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
     pages = torch.zeros((inp.num_pages, FP8_PAGE_BYTES), dtype=torch.uint8, device="cuda")

@@ -315,7 +315,7 @@ def test_pages_past_4_gib():
     torch.cuda.empty_cache()
 
 
-def test_mismatched_plan_writes_nan_lse_and_nothing_else():
+def test_mismatched_plan_writes_nan_lse_and_nothing_else(plan_override):
     """A plan built for other arguments, passed through the C ABI (the Python
     binding refuses it first): the decode kernel finds the header mismatch
     before it reads anything else, writes NaN into every lse entry and stores
@@ -333,15 +333,18 @@ def test_mismatched_plan_writes_nan_lse_and_nothing_else():
     cases = [  # (tag, plan h_q, plan partitions, call h_q, call partitions, fp8 call)
         ("partition count", 64, 128, 64, 64, False),
         ("row blocks", 64, 64, 128, 64, False),
-        ("BF16 plan into the FP8 call", 64, 64, 64, 64, True),
+        # forced onto the score/value organisation, 32 rows take 32-row
+        # blocks over BF16 and 64-row blocks over FP8: the plans differ
+        ("BF16 plan into the FP8 call", 32, 64, 32, 64, True),
         ("16-row plan, other partition count", 16, 64, 16, 32, False),
     ]
     for tag, ph, pp, ch, cp, fp8 in cases:
+        plan_override(kernel="ws" if fp8 else None)
         meta = mla.get_split_metadata(sl, ph, 1, pp)
         host = meta.metadata.cpu().numpy()
         assert _lib.lib().mla_check_metadata_host(host.ctypes.data, host.nbytes, inp.batch, ch, 1, cp,
                                                   int(fp8)) == 1, tag
-        qc = q if ch == 64 else torch.cat([q, q], dim=2).contiguous()
+        qc = q if ch == 64 else torch.cat([q, q], dim=2).contiguous() if ch == 128 else q[:, :, :ch].contiguous()
         out = torch.full((inp.batch, 1, ch, 512), 1.5, dtype=torch.bfloat16, device="cuda")
         lse = torch.zeros((inp.batch, 1, ch), dtype=torch.float32, device="cuda")
         ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
