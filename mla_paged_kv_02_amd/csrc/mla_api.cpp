@@ -111,7 +111,8 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     // stream each page once per 128 rows, but one wave per SIMD keeps too few
     // LDS reads in flight: at 128 heads they are 13-15% slower than two
     // 64-row blocks. The FP8 cache has the same split: 16-row blocks below 64
-    // rows, 64-row score/value blocks (with the FP8 fill) from 64 rows on.
+    // rows, 64-row score/value blocks (reading the E4M3 cache as it is) from
+    // 64 rows on.
     const int ov = g_kernel_override.load(std::memory_order_relaxed);
     DecodeKernel k;
     if (fp8) {

@@ -46,22 +46,25 @@
 // FP8 latent cache (64-row blocks; page layout of mla_decode_fp8.h: four
 // 16-token groups, each its E4M3 latent rows, BF16 rotary rows and FP32
 // per-token scales; latent coordinate d of token t is e4m3 * scale[t]). The
-// ring keeps exactly the BF16 slot layout above, so both products read it
-// unchanged; what differs is how a slot is filled and where the scale goes:
+// pipeline, the roles and the barriers are the BF16 ones; what differs is
+// what a ring slot holds and how the products read it:
 //
-//  * value wave v loads rows 8v..8v+7 of a half page (latent bytes, rotary
-//    row, scale) into registers at the end of the step two before the one
-//    that scores it, and at the end of the step before, converts the latent
-//    bytes to BF16 (exact: every E4M3 value is a BF16 value), writes them,
-//    the rotary part and the scale into the half page's slot and loads the
-//    next half page into the same registers; each half page is converted
-//    once per workgroup;
-//  * the score waves keep the latent and rotary parts of a score apart
-//    (latent k-steps, then the two rotary k-steps) and combine them as
-//    scale * latent + rotary; the value product sees p_t * scale_t, the
-//    normaliser sums p_t.
-// These loads are ordinary ones, tracked and waited for by the compiler; the
-// kernel issues no untracked load in this mode.
+//  * a slot holds the half page as it is in memory, still E4M3 (21 KB
+//    instead of 36 KB): the value waves fill it with the same untracked
+//    16-byte direct loads, two half pages ahead, placing latent rows at a
+//    528-byte stride (a row's 16-byte gap holds four rows' scales) and
+//    permuting rotary chunks, so that both products read without bank
+//    conflicts and with constant offsets;
+//  * score waves read 8 latent bytes per k-step and widen them to BF16 in
+//    registers (exact: every E4M3 value is a BF16 value); they keep the
+//    latent and rotary parts of a score apart and combine them as
+//    scale * latent + rotary;
+//  * value waves read V^T with the byte-transposing LDS read (8 keys of one
+//    dimension per lane) and widen it the same way; P crosses over with its
+//    keys in the read's byte order, and holds p_t * scale_t (the
+//    normaliser sums p_t).
+// So HBM, LDS writes and the LDS reads of both products carry half the
+// bytes of the BF16 path, and nothing is converted twice.
 #include "mla_common.h"
 #include "mla_fused_combine.h"
 #include "mla_internal.h"
@@ -94,40 +97,50 @@ constexpr float kRefMargin = 32.f;
 constexpr float kHeadroom = 64.f;
 
 // FP8 page: four groups of 16 tokens, each 16 E4M3 latent rows (512 B), 16
-// BF16 rotary rows (128 B) and 16 FP32 scales
+// BF16 rotary rows (128 B) and 16 FP32 scales; a half page is two whole
+// groups, 20608 contiguous bytes
 constexpr int kF8Group = 16 * 512 + 16 * 128 + 16 * 4;   // 10304
 constexpr int kF8PageBytes = 4 * kF8Group;                 // 41216
+constexpr int kF8HalfBytes = 2 * kF8Group;                 // 20608
 constexpr int kF8RopeOff = 16 * 512;
 constexpr int kF8ScaleOff = 16 * 512 + 16 * 128;
+// FP8 ring slot: a half page as loaded, still E4M3. Latent rows of 512 B at
+// a stride of 528 B (16 rows at the same column fall on 16 different 16-byte
+// bank groups), the 16-byte gap after latent row k < 8 holding the scales of
+// rows 4k..4k+3; then the 32 rotary rows of 128 B, chunk c of row r at chunk
+// slot c ^ ((r >> 1) & 7). 21 wave-loads of 1 KB fill it (the end of the
+// last one is padding).
+constexpr int kF8LatStride = 528;
+constexpr int kF8LdsRope = kCRows * kF8LatStride;   // 16896
+constexpr int kF8SlotLoads = 21;
+constexpr int kF8Slot = kF8SlotLoads * 1024;        // 21504
+constexpr int kF8Mine = (kF8SlotLoads + 3) / 4;     // 6: value wave v issues loads v, v+4, ..
+static_assert(kF8LdsRope + kCRows * 128 <= kF8Slot, "FP8 slot layout");
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// A value-wave lane's share of one half page of the FP8 cache: 64 latent
-// bytes (row 8v + lane/8, bytes 64 (lane % 8) ..), 16 rotary bytes of the
-// same row (bytes 16 (lane % 8) ..) and the row's scale.
-struct F8Part {
-    u32x4 lat[4];
-    u32x4 rope;
-    float sc;
-};
+// 8 E4M3 values (byte k = element k) -> 8 BF16 values, exact (every E4M3
+// value is a BF16 value)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(const u32x2& w) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
 
-// 16 E4M3 values -> 16 BF16 values, exact (every E4M3 value is a BF16 value)
-__device__ __forceinline__ void e4m3x16_to_bf16_ws(const u32x4& w, bf16x8& lo, bf16x8& hi) {
-    bf16x2 p[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        p[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false);
-        p[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lo[2 * i] = p[i][0];
-        lo[2 * i + 1] = p[i][1];
-        hi[2 * i] = p[4 + i][0];
-        hi[2 * i + 1] = p[4 + i][1];
-    }
+__device__ __forceinline__ u32x2 lds_read8(const uint8_t* p) { return *(const MLA_AS3 u32x2*)(p); }
+
+// Transposing LDS read of bytes: in each group of 16 lanes, lane 2k + h
+// addresses bytes 8h..8h+7 of row k of an 8 x 16 block of bytes, and lane n
+// receives column n of the block (byte k from row k).
+__device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_AS3 i32x2*)(p)));
 }
 
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
@@ -162,8 +175,14 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     constexpr int kRows = Sh::kRows;
     constexpr int kSW = Sh::kScoreWaves;
     constexpr int kPBytes = kRT * 1024;
+    constexpr int kSlot = kFp8 ? kF8Slot : kCBytes;
+    // ring slots, and how many half pages ahead of the one being scored the
+    // value waves load (over the FP8 cache six slots, loading four ahead,
+    // measured no faster: 190 vs 192 us at 128 heads, 4096 tokens)
+    constexpr int kNS = 4;
+    constexpr int kDist = kNS - 2;
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[4 * kCBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kNS * kSlot];
     // weights of a half page for the value waves: row tile rt at 1 KB * rt,
     // lane l at 16 l (the B operand of O^T += V^T P^T); two buffers by parity
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kPBytes];
@@ -175,8 +194,6 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     // by every wave after the next barrier
     __shared__ int restart_flag[2];
     __shared__ int last_flag;   // this workgroup merges a split sequence
-    // FP8: the per-token scales of the half page in each ring slot
-    __shared__ __attribute__((aligned(16))) float slot_scale[kFp8 ? 4 : 1][kCRows];
 
     if (!plan_matches_or_poison<Sh::kThreads>(a)) return;
     const int lane = threadIdx.x & 63;
@@ -264,46 +281,80 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     // load j of the taken half page into the slot at `dst`. Rows at or past
     // the sequence end read the page's first kilobyte (row 0, always
     // valid): finite data whose softmax weight is zero.
-    auto issue_one = [&](uint32_t dst, int j) {
+    auto issue_bf16 = [&](uint32_t dst, int j) {
         const int base = t_half * kCBytes + sw * 9216;
         const int r = t_half * kCRows + sw * 8 + (j * 64 + lane) / kRowChunks;
         const uint32_t off = r < t_rows ? (uint32_t)(base + goff[j]) : (uint32_t)(lane * 16);
         load_lds16_untracked(t_src, off, dst + sw * 9216 + j * 1024);
     };
-    auto issue_all = [&](uint32_t dst) {
-#pragma unroll
-        for (int j = 0; j < kWLoads; ++j) issue_one(dst, j);
-    };
 
-    // ---- FP8 (value waves): rows 8 sw .. 8 sw + 7 of the taken half page
-    // into registers, and from registers into a ring slot. Rows at or past
-    // the sequence end read row 0 of the page (a written token: finite).
-    const int f8_hr = 8 * sw + (lane >> 3);   // the lane's row of the half page
-    auto f8_load = [&](F8Part& fp) {
-        const int prow = t_half * kCRows + f8_hr;
-        const int srow = prow < t_rows ? prow : 0;
-        const uint8_t* gb = t_src + (srow >> 4) * kF8Group;
-        const int i = srow & 15;
+    // FP8: this wave's loads of a slot are numbers sw + 4 i (i < 6 for value
+    // wave 0, i < 5 for the others; 21 in all), lane l of load j filling
+    // chunk position 64 j + l of the slot. f8_src[i]: that chunk's source
+    // offset in the half page. f8_alt[i]: 64 * (source offset in the page of
+    // the same chunk of the page's row 0) + 1 + (the chunk's row of the half
+    // page), or 0 for a chunk read as it is (scales, padding). Rows at or
+    // past the sequence end read row 0 of the page (a written token: finite);
+    // their scales are read as they are and never used.
+    int f8_src[kF8Mine], f8_alt[kF8Mine];
+    if constexpr (kFp8) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            fp.lat[k] = *reinterpret_cast<const u32x4*>(gb + i * 512 + (lane & 7) * 64 + 16 * k);
-        fp.rope = *reinterpret_cast<const u32x4*>(gb + kF8RopeOff + i * 128 + (lane & 7) * 16);
-        fp.sc = *reinterpret_cast<const float*>(gb + kF8ScaleOff + i * 4);
-    };
-    auto f8_store = [&](const F8Part& fp, int slot) {
-        uint8_t* row = ring + slot * kCBytes + f8_hr * kRowBytes;
-        const int swz = lds_swizzle(f8_hr);
-        const int c0 = 8 * (lane & 7);   // the lane's first latent chunk (8 BF16 each)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            bf16x8 lo, hi;
-            e4m3x16_to_bf16_ws(fp.lat[k], lo, hi);
-            *reinterpret_cast<bf16x8*>(row + (((c0 + 2 * k) ^ swz) << 4)) = lo;
-            *reinterpret_cast<bf16x8*>(row + (((c0 + 2 * k + 1) ^ swz) << 4)) = hi;
+        for (int i = 0; i < kF8Mine; ++i) {
+            const int pos = (sw + 4 * i) * 64 + lane;
+            int src = 0, alt = 0;
+            if (pos < kF8LdsRope / 16) {
+                const int r = pos / (kF8LatStride / 16);
+                const int q = pos - r * (kF8LatStride / 16);
+                if (q < 32) {
+                    src = (r >> 4) * kF8Group + (r & 15) * 512 + 16 * q;
+                    alt = ((16 * q) << 6) + 1 + r;
+                } else if (r < 8) {
+                    // scales of rows 4r..4r+3 (one group)
+                    src = (r >> 2) * kF8Group + kF8ScaleOff + 16 * (r & 3);
+                }
+            } else if (pos < (kF8LdsRope + kCRows * 128) / 16) {
+                const int pp = pos - kF8LdsRope / 16;
+                const int r = pp >> 3;
+                const int c = (pp & 7) ^ ((r >> 1) & 7);
+                src = (r >> 4) * kF8Group + kF8RopeOff + (r & 15) * 128 + 16 * c;
+                alt = ((kF8RopeOff + 16 * c) << 6) + 1 + r;
+            }
+            f8_src[i] = src;
+            f8_alt[i] = alt;
         }
-        const int rc = kHeadDimV / 8 + (lane & 7);   // rotary chunk 64..71
-        *reinterpret_cast<u32x4*>(row + ((rc ^ swz) << 4)) = fp.rope;
-        if ((lane & 7) == 0) slot_scale[kFp8 ? slot : 0][f8_hr] = fp.sc;
+    }
+    auto issue_fp8 = [&](uint32_t dst, int i) {
+        const int r = (f8_alt[i] & 63) - 1;
+        const uint32_t off = (r < 0 || t_half * kCRows + r < t_rows) ? (uint32_t)(t_half * kF8HalfBytes + f8_src[i])
+                                                                     : (uint32_t)(f8_alt[i] >> 6);
+        load_lds16_untracked(t_src, off, dst + (sw + 4 * i) * 1024);
+    };
+    // this wave's i-th load of the taken half page into the slot at `dst`
+    auto issue_one = [&](uint32_t dst, int i) {
+        if constexpr (kFp8) issue_fp8(dst, i);
+        else issue_bf16(dst, i);
+    };
+    auto issue_all = [&](uint32_t dst) {
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int i = 0; i < kF8Mine - 1; ++i) issue_fp8(dst, i);
+            if (sw == 0) issue_fp8(dst, kF8Mine - 1);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kWLoads; ++j) issue_bf16(dst, j);
+        }
+    };
+    // wait for the oldest slot in flight, `younger` slots' loads having been
+    // issued after it
+    auto wait_oldest = [&](int younger) {
+        static_assert(kDist == 2, "waits for up to one younger slot");
+        if (younger <= 0) wait_then_fence<kWaitAll>();
+        else if constexpr (kFp8) {
+            if (sw == 0) wait_then_fence<wait_vm_lgkm0(kF8Mine)>();
+            else wait_then_fence<wait_vm_lgkm0(kF8Mine - 1)>();
+        } else {
+            wait_then_fence<kWaitSlot>();
+        }
     };
 
     // per-lane LDS offsets inside a slot: K fragment of k-step ks for key row
@@ -340,30 +391,22 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
         f32x4 o[kScorer ? 1 : kRT][kScorer ? 1 : kVTiles];
 
         // value waves: the stream's first two half pages
-        bool issued_next = false;   // the half page after the one waited for is in flight
-        // FP8: the stream's next half page not yet in the ring, in registers
-        F8Part f8;
-        bool f8_got = false;
-        // FP8 (value waves): write the stream's next half page into slot
-        // `slot` and load the one after it
-        auto f8_prime = [&](int slot) {
-            if (take()) {
-                f8_load(f8);
-                f8_store(f8, slot);
+        // value waves: half pages of the stream issued and not yet scored
+        int nq = 0;
+        // fill slots soff, soff+1, .. with the stream's next kDist half pages
+        auto prime = [&](int soff0) {
+            nq = 0;
+            for (int k = 0; k < kDist; ++k) {
+                if (!take()) break;
+                issue_all(ring_lds + ((soff0 + k) % kNS) * kSlot);
+                ++nq;
             }
-            f8_got = take();
-            if (f8_got) f8_load(f8);
         };
-        if constexpr (kFp8 && !kScorer) {
+        if constexpr (!kScorer) {
             if (fseg.b >= 0) fpage = fpage_of();
-            f8_prime(0);
-        } else if constexpr (!kScorer) {
-            if (fseg.b >= 0) fpage = fpage_of();
-            if (take()) issue_all(ring_lds);
-            issued_next = take();
-            if (issued_next) issue_all(ring_lds + kCBytes);
+            prime(0);
         }
-        int soff = 0;   // ring slot of the segment's first half page (0 or 2)
+        int soff = 0;   // ring slot of the segment's first half page
 
         Seg seg = find_seg(b0, n0);
         while (seg.b >= 0) {
@@ -413,33 +456,30 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                 bool skip = false;   // overflow seen: no more weights until the restart
 
                 // Step c: the value waves take the stream's next half page (this
-                // segment's half page c+2, or the next segment's first two) into
-                // slot (soff+c+2) % 4 (its previous contents, half page c-2, were
-                // accumulated in step c-1) and accumulate half page c-1 from slot
-                // (soff+c+3) % 4, while the score waves turn half page c (slot
-                // (soff+c) % 4) into weights. The last step, c = nch, only
-                // accumulates.
+                // segment's half page c+kDist, or one of the next segments')
+                // into slot (soff+c+kDist) % kNS (its previous contents, half
+                // page c-2, were accumulated in step c-1) and accumulate half
+                // page c-1 from slot (soff+c-1) % kNS, while the score waves
+                // turn half page c (slot (soff+c) % kNS) into weights. The last
+                // step, c = nch, only accumulates.
                 int c = 0;
                 auto step = [&](auto sc) -> bool {
                     constexpr int S = decltype(sc)::value;
-                    const uint8_t* slot_cur = ring + ((S + soff) & 3) * kCBytes;
-                    if constexpr (!kScorer && !kFp8) {
-                        // my part of half page c (at most the next one's loads are younger)
-                        if (c < nch) {
-                            if (issued_next) wait_then_fence<kWaitSlot>();
-                            else wait_then_fence<kWaitAll>();
-                        }
+                    const unsigned rpos = (unsigned)(soff + c);
+                    const uint8_t* slot_cur = ring + (rpos % kNS) * kSlot;
+                    if constexpr (!kScorer) {
+                        // my part of half page c (the loads of the nq - 1 half
+                        // pages after it are younger)
+                        if (c < nch) wait_oldest(nq - 1);
                     }
                     block_barrier();   // publishes the weights and flags of step c-1
                     if (restart_flag[(S + 1) & 1] != 0) return false;   // raised in step c-1
                     bool issue_now = false;
                     uint32_t dst = 0;
                     if constexpr (!kScorer) {
-                        if constexpr (!kFp8) {
-                            issue_now = c < nch && take();
-                            dst = ring_lds + ((S + soff + 2) & 3) * kCBytes;
-                            if (c == 0 && issue_now) issue_all(dst);
-                        }
+                        issue_now = c < nch && take();
+                        dst = ring_lds + ((rpos + kDist) % kNS) * kSlot;
+                        if (c == 0 && issue_now) issue_all(dst);
                     } else if (c < nch) {
                         // FP8: the per-token scales of this wave's keys (folded into P)
                         f32x4 my_scale = {1.f, 1.f, 1.f, 1.f};
@@ -448,7 +488,6 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                         // all. Lane holds keys key0 + j (j < 4) of rows lrow[r],
                         // -inf where masked; lm[r] = the lane's maximum of them.
                         auto score_tile = [&](int tile, f32x4 (&sv)[NR], float (&lm)[NR]) {
-                            const uint8_t* kb = slot_cur + tile * 16 * kRowBytes;
                             f32x4 sp[NR][2];
                             f32x4 slat[NR];   // FP8: the latent part, scaled below
 #pragma unroll
@@ -456,30 +495,61 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
 #pragma unroll
                                 for (int pp = 0; pp < 2; ++pp) sp[r][pp] = f32x4{0.f, 0.f, 0.f, 0.f};
                             constexpr int KD = 4;
-                            auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
-                            bf16x8 kf[KD];
+                            if constexpr (kFp8) {
+                                // latent k-step ks: bytes 32 ks + 8 g .. +7 of key row
+                                // 16 tile + i16, widened to BF16 in registers
+                                const uint8_t* kl = slot_cur + (tile * 16 + i16) * kF8LatStride + 8 * g;
+                                u32x2 kw[KD];
 #pragma unroll
-                            for (int d = 0; d < KD; ++d) kf[d] = lds_read16(kb + k_off(d));
+                                for (int d = 0; d < KD; ++d) kw[d] = lds_read8(kl + 32 * d);
+                                // rotary k-steps: chunk 4 j + g of rotary row 16 tile + i16
+                                const uint8_t* kr = slot_cur + kF8LdsRope + (tile * 16 + i16) * 128;
+                                const int rsw = (i16 >> 1) & 7;
+                                bf16x8 krf[2];
 #pragma unroll
-                            for (int ks = 0; ks < kKS; ++ks) {
-                                if (kFp8 && ks == kHeadDimV / 32) {
-                                    // latent k-steps done: keep them, accumulate the rotary part apart
-#pragma unroll
-                                    for (int r = 0; r < NR; ++r) {
-                                        slat[r] = sp[r][0] + sp[r][1];
-                                        sp[r][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                                        sp[r][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                                for (int ks = 0; ks < kHeadDimV / 32; ++ks) {
+                                    const bf16x8 kf = e4m3x8_to_bf16(kw[ks % KD]);
+                                    if (ks + KD < kHeadDimV / 32) kw[ks % KD] = lds_read8(kl + 32 * (ks + KD));
+                                    if (ks == kHeadDimV / 32 - KD) {
+                                        krf[0] = lds_read16(kr + ((g ^ rsw) << 4));
+                                        krf[1] = lds_read16(kr + (((4 + g) ^ rsw) << 4));
                                     }
-                                }
 #pragma unroll
-                                for (int r = 0; r < NR; ++r) sp[r][ks & 1] = mfma16(kf[ks % KD], qf[r][ks], sp[r][ks & 1]);
-                                if (ks + KD < kKS) kf[ks % KD] = lds_read16(kb + k_off(ks + KD));
-                                __builtin_amdgcn_sched_barrier(0);
+                                    for (int r = 0; r < NR; ++r) sp[r][ks & 1] = mfma16(kf, qf[r][ks], sp[r][ks & 1]);
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
+                                // keep the latent part, accumulate the rotary part apart
+#pragma unroll
+                                for (int r = 0; r < NR; ++r) {
+                                    slat[r] = sp[r][0] + sp[r][1];
+                                    sp[r][0] = mfma16(krf[0], qf[r][kHeadDimV / 32], f32x4{0.f, 0.f, 0.f, 0.f});
+                                    sp[r][1] = mfma16(krf[1], qf[r][kHeadDimV / 32 + 1], f32x4{0.f, 0.f, 0.f, 0.f});
+                                }
+                            } else {
+                                const uint8_t* kb = slot_cur + tile * 16 * kRowBytes;
+                                auto k_off = [&](int ks) { return kofs[ks & 1] + (ks >> 1) * 128; };
+                                bf16x8 kf[KD];
+#pragma unroll
+                                for (int d = 0; d < KD; ++d) kf[d] = lds_read16(kb + k_off(d));
+#pragma unroll
+                                for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+                                    for (int r = 0; r < NR; ++r)
+                                        sp[r][ks & 1] = mfma16(kf[ks % KD], qf[r][ks], sp[r][ks & 1]);
+                                    if (ks + KD < kKS) kf[ks % KD] = lds_read16(kb + k_off(ks + KD));
+                                    __builtin_amdgcn_sched_barrier(0);
+                                }
                             }
                             const int key0 = (lo + c / 2) * kPageRows + (c & 1) * kCRows + tile * 16 + 4 * g;
                             f32x4 sck = {0.f, 0.f, 0.f, 0.f};
-                            if constexpr (kFp8)
-                                sck = *reinterpret_cast<const f32x4*>(&slot_scale[kFp8 ? (S + soff) & 3 : 0][tile * 16 + 4 * g]);
+                            if constexpr (kFp8) {
+                                // scales of keys 16 tile + 4 g + j: chunk 4 tile + g of the
+                                // scale chunks; those of rows past the sequence end are
+                                // whatever the page holds there, replaced by 0
+                                sck = *reinterpret_cast<const f32x4*>(slot_cur + (4 * tile + g) * kF8LatStride + 512);
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) sck[j] = key0 + j < nseq ? sck[j] : 0.f;
+                            }
 #pragma unroll
                             for (int r = 0; r < NR; ++r) {
                                 float m = -INFINITY;
@@ -543,55 +613,76 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                                     pw[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r][j], a.scale_log2, neg_m));
                                     l_run[r] += pw[j];
                                 }
-                                // B = P^T of row tile rt0 + r: k-slot 4 kt + j <-> key 16 kt + 4 g + j;
-                                // FP8: the value product sees p_t * scale_t, the sum p_t alone
-                                if constexpr (kFp8) pw *= my_scale;
-                                *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(rt0 + r) * 1024 + lane * 16 + kt * 8]) =
-                                    pack_bf16x4(pw);
+                                // B = P^T of row tile rt0 + r. BF16: k-slot 4 kt + j of lane
+                                // group g <-> key 16 kt + 4 g + j. FP8: k-slot k of lane group
+                                // g' <-> key 8 g' + k (the byte order of the transposing
+                                // read), and the value product sees p_t * scale_t, the
+                                // sum p_t alone.
+                                if constexpr (kFp8) {
+                                    pw *= my_scale;
+                                    *reinterpret_cast<bf16x4*>(
+                                        &pbuf[S & 1][(rt0 + r) * 1024 + ((2 * kt + (g >> 1)) * 16 + i16) * 16 + 8 * (g & 1)]) =
+                                        pack_bf16x4(pw);
+                                } else {
+                                    *reinterpret_cast<bf16x4*>(&pbuf[S & 1][(rt0 + r) * 1024 + lane * 16 + kt * 8]) =
+                                        pack_bf16x4(pw);
+                                }
                             }
                         }
                     }
                     if (!kScorer && c >= 1) {
                         // ---- O^T += V^T P^T for half page c-1: the row tiles
-                        // share each V^T fragment (two transposing reads)
-                        const uint8_t* cur = ring + ((S + soff + 3) & 3) * kCBytes;
+                        // share each V^T fragment
+                        const uint8_t* cur = ring + ((rpos + kNS - 1) % kNS) * kSlot;
                         const uint8_t* pb = &pbuf[(S + 1) & 1][lane * 16];
                         bf16x8 pf[kRT];
 #pragma unroll
                         for (int rt = 0; rt < kRT; ++rt) pf[rt] = lds_read16(pb + rt * 1024);
-                        constexpr int VD = kFp8 ? 3 : 5;
-                        auto v_frag = [&](int t) {
-                            const int dt = sw * kVTiles + t;
-                            const int off = vofs[dt & 3] + (dt >> 2) * 128;
-                            return cat_bf16x4(lds_read_tr(cur + off), lds_read_tr(cur + 16 * kRowBytes + off));
-                        };
-                        bf16x8 vf[VD];
+                        if constexpr (kFp8) {
+                            // V^T fragment of value tile dt: one transposing byte read,
+                            // lane (i16, g) receiving dims 16 dt + i16 of key rows
+                            // 8 g .. 8 g + 7, widened to BF16 in registers
+                            const uint8_t* vb =
+                                cur + (8 * g + (i16 >> 1)) * kF8LatStride + 8 * (i16 & 1) + 16 * kVTiles * sw;
+                            constexpr int VD = 4;
+                            u32x2 vw[VD];
 #pragma unroll
-                        for (int d = 0; d < VD; ++d) vf[d] = v_frag(d);
+                            for (int d = 0; d < VD; ++d) vw[d] = lds_read_tr8(vb + 16 * d);
 #pragma unroll
-                        for (int t = 0; t < kVTiles; ++t) {
+                            for (int t = 0; t < kVTiles; ++t) {
+                                const bf16x8 vf = e4m3x8_to_bf16(vw[t % VD]);
+                                if (t + VD < kVTiles) vw[t % VD] = lds_read_tr8(vb + 16 * (t + VD));
 #pragma unroll
-                            for (int rt = 0; rt < kRT; ++rt) o[rt][t] = mfma16(vf[t % VD], pf[rt], o[rt][t]);
-                            if (t + VD < kVTiles) vf[t % VD] = v_frag(t + VD);
-                            if (issue_now) issue_one(dst, t);
-                            __builtin_amdgcn_sched_barrier(0);
+                                for (int rt = 0; rt < kRT; ++rt) o[rt][t] = mfma16(vf, pf[rt], o[rt][t]);
+                                if (issue_now && t < kF8Mine - 1) issue_one(dst, t);
+                                if (issue_now && t == kF8Mine - 1 && sw == 0) issue_one(dst, t);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                        } else {
+                            // two transposing reads per V^T fragment
+                            constexpr int VD = 5;
+                            auto v_frag = [&](int t) {
+                                const int dt = sw * kVTiles + t;
+                                const int off = vofs[dt & 3] + (dt >> 2) * 128;
+                                return cat_bf16x4(lds_read_tr(cur + off), lds_read_tr(cur + 16 * kRowBytes + off));
+                            };
+                            bf16x8 vf[VD];
+#pragma unroll
+                            for (int d = 0; d < VD; ++d) vf[d] = v_frag(d);
+#pragma unroll
+                            for (int t = 0; t < kVTiles; ++t) {
+#pragma unroll
+                                for (int rt = 0; rt < kRT; ++rt) o[rt][t] = mfma16(vf[t % VD], pf[rt], o[rt][t]);
+                                if (t + VD < kVTiles) vf[t % VD] = v_frag(t + VD);
+                                if (issue_now) issue_one(dst, t);
+                                __builtin_amdgcn_sched_barrier(0);
+                            }
+                            static_assert(kVTiles + 1 == kWLoads, "one load per value tile and one after");
+                            if (issue_now) issue_one(dst, kVTiles);
                         }
-                        static_assert(kVTiles + 1 == kWLoads, "one load per value tile and one after");
-                        if (issue_now) issue_one(dst, kVTiles);
                     }
                     if constexpr (!kScorer) {
-                        if (c < nch) issued_next = issue_now;
-                    }
-                    if constexpr (kFp8 && !kScorer) {
-                        // the stream's next half page (loaded at the end of
-                        // the step before) into its slot, which the value
-                        // waves left two steps ago (the next barrier publishes
-                        // it), then the one after it into the registers
-                        if (c < nch) {
-                            if (f8_got) f8_store(f8, (S + soff + 1) & 3);
-                            f8_got = take();
-                            if (f8_got) f8_load(f8);
-                        }
+                        if (c < nch) nq += issue_now ? 0 : -1;
                     }
                     ++c;
                     return c <= nch;
@@ -630,22 +721,13 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
 #pragma unroll
                         for (int r = 0; r < NR; ++r) m_ref[r] = row_m[lrow[r]];
                     }
-                    if constexpr (kFp8 && !kScorer) {
-                        // restart the stream at this segment's start and
-                        // write its first half page again
-                        fseg = seg;
-                        fc = 0;
-                        fpage = fpage_of();
-                        f8_prime(soff);
-                    } else if constexpr (!kScorer) {
+                    if constexpr (!kScorer) {
                         // drain the ring and refill it from this segment's start
                         wait_then_fence<kWaitAll>();
                         fseg = seg;
                         fc = 0;
                         fpage = fpage_of();
-                        if (take()) issue_all(ring_lds + soff * kCBytes);
-                        issued_next = take();
-                        if (issued_next) issue_all(ring_lds + (soff + 1) * kCBytes);
+                        prime(soff);
                     }
                     block_barrier();   // every wave has read the flags and row_m
                 }
@@ -705,7 +787,7 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
             block_barrier();   // row_m, row_l and the buffers are free again
             if (!full && a.counters)
                 count_partial_and_combine<Sh::kThreads, kRows, (kRT == 4 ? 512 : 256)>(a, b, rb, &last_flag);
-            soff = (soff + nch) & 3;
+            soff = (soff + nch) % kNS;
             seg = find_seg(b + 1, 0);
         }
         if (a.counters) write_empty_sequences<Sh::kThreads>(a);
