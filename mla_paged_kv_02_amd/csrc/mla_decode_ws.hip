@@ -181,8 +181,15 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
     // measured no faster: 190 vs 192 us at 128 heads, 4096 tokens)
     constexpr int kNS = 4;
     constexpr int kDist = kNS - 2;
+    // 64-row blocks: the first segment's query block is staged from slot 2
+    // on (rows of 1152 B, chunks placed as in a BF16 slot) before the ring
+    // reaches those slots
+    constexpr bool kQStage = kRT == 4;
+    constexpr int kQOff = 2 * kSlot;
+    constexpr int kRingBytes = kQStage && kQOff + kRows * kRowBytes > kNS * kSlot ? kQOff + kRows * kRowBytes
+                                                                                : kNS * kSlot;
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kNS * kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingBytes];
     // weights of a half page for the value waves: row tile rt at 1 KB * rt,
     // lane l at 16 l (the B operand of O^T += V^T P^T); two buffers by parity
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][kPBytes];
@@ -402,10 +409,47 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
                 ++nq;
             }
         };
+        // The first segment's query block (64-row blocks): wave w brings rows
+        // 8w..8w+7 into the staging area with direct loads (each byte of the
+        // block crosses the memory pipeline once; rows past M read row 0 of
+        // the block), ahead of the ring's first half pages.
+        const bool q_staged = kQStage && fseg.b >= 0;
+        if (q_staged) {
+            const uint16_t* q_blk = a.q + ((size_t)fseg.b * a.M + rb * kRows) * kHeadDim;
+#pragma unroll
+            for (int j = 0; j < kWLoads; ++j) {
+                const int rl = (j * 64 + lane) / kRowChunks;
+                const int row = 8 * wid + rl;
+                const int srow = rb * kRows + row < a.M ? row : 0;
+                load_lds16_untracked(q_blk, (uint32_t)(srow * kRowBytes + goff[j] - rl * kRowBytes),
+                                     ring_lds + kQOff + wid * 9216 + j * 1024);
+            }
+        }
         if constexpr (!kScorer) {
             if (fseg.b >= 0) fpage = fpage_of();
             prime(0);
         }
+        if (q_staged) {
+            // every wave's query loads have landed (a value wave's are older
+            // than the nq slots of the prime) before the barrier publishes them
+            if constexpr (kScorer) {
+                wait_then_fence<kWaitAll>();
+            } else if (nq <= 0) {
+                wait_then_fence<kWaitAll>();
+            } else if (nq == 1) {
+                wait_oldest(1);
+            } else {
+                static_assert(kDist == 2, "the prime fills at most two slots");
+                if constexpr (kFp8) {
+                    if (sw == 0) wait_then_fence<wait_vm_lgkm0(2 * kF8Mine)>();
+                    else wait_then_fence<wait_vm_lgkm0(2 * (kF8Mine - 1))>();
+                } else {
+                    wait_then_fence<wait_vm_lgkm0(2 * kWLoads)>();
+                }
+            }
+            block_barrier();
+        }
+        bool q_in_lds = q_staged;
         int soff = 0;   // ring slot of the segment's first half page
 
         Seg seg = find_seg(b0, n0);
@@ -428,14 +472,26 @@ __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(D
             const int slotno =
                 full ? 0 : ld_const_ws(seqinfo, 4 * b + 0) + (p - ld_const_ws(seqinfo, 4 * b + 1));
             if constexpr (kScorer) {
+                if (kQStage && q_in_lds) {
+                    // from the staging area: row lrow[r] (its low three bits are
+                    // those of i16, so the chunk placement is that of kofs)
 #pragma unroll
-                for (int r = 0; r < NR; ++r) {
-                    const uint16_t* qp = a.q +
-                        ((size_t)b * a.M + (srow_ok[r] ? rb * kRows + lrow[r] : rb * kRows)) * kHeadDim + g * 8;
+                    for (int r = 0; r < NR; ++r) {
+                        const uint8_t* qr = ring + kQOff + (lrow[r] - i16) * kRowBytes;
 #pragma unroll
-                    for (int ks = 0; ks < kKS; ++ks) qf[r][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+                        for (int ks = 0; ks < kKS; ++ks) qf[r][ks] = lds_read16(qr + kofs[ks & 1] + (ks >> 1) * 128);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NR; ++r) {
+                        const uint16_t* qp = a.q +
+                            ((size_t)b * a.M + (srow_ok[r] ? rb * kRows + lrow[r] : rb * kRows)) * kHeadDim + g * 8;
+#pragma unroll
+                        for (int ks = 0; ks < kKS; ++ks) qf[r][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+                    }
                 }
             }
+            q_in_lds = false;
 
             bool restart = false;
             do {
