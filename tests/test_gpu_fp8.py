@@ -58,6 +58,9 @@ FP8_CASES = [
     ([2, 3, 65, 190], 2, 128, True),
     ([150, 3, 1000, 64, 0], 8, 128, True),
     ([300, 2, 77], 16, 64, False),
+    # 64-row blocks whose last block is partly past M (M = 80, M = 120)
+    ([130, 70, 3], 1, 80, False),
+    ([1, 200, 65], 3, 40, True),
 ]
 
 

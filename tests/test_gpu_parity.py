@@ -48,6 +48,9 @@ SMALL_CASES = [
     ([500, 20, 64, 0], 64, 16, True),
     ([300, 2, 77], 16, 64, False),
     ([40, 129], 32, 8, True),
+    # 64-row blocks whose last block is partly past M (M = 80, M = 120)
+    ([130, 70, 3], 1, 80, False),
+    ([200, 64], 3, 40, True),
 ]
 
 
