@@ -159,15 +159,17 @@ bool make_plan(int batch, int h_q, int s_q, int num_partitions, int num_cus, Pla
     pl.cseg = 1 + tm / 16;
     pl.slots = 2 * pl.P;
     // With no more partitions than sequences most sequences sit in one
-    // partition and the few split ones have about two partials: below 128
+    // partition and the few split ones have about two partials: up to 128
     // rows the merge then runs in the decode kernel and the call is one
-    // kernel. With more partitions per sequence the merging workgroups'
-    // extra reads land on the critical path, and from 128 rows the partials
-    // are large enough that writing them through to the coherent level costs
-    // more than a second kernel (128 heads, 128 sequences of 4096 tokens:
-    // call 186-190 vs 192-195 us); a combine kernel merges them instead
-    // (mla_set_plan_override can force either).
-    pl.fused_combine = pl.P <= pl.batch && pl.M < 128;
+    // kernel (128 heads, 128 sequences of 4096 tokens, none split: step
+    // 212 vs 217 us). With more partitions per sequence the merging
+    // workgroups' extra reads land on the critical path, and beyond 128 rows
+    // the partials are large enough that writing them through to the
+    // coherent level costs more than a second kernel (two tokens at 128
+    // heads over 132 sequences of 1-8192 tokens, 60 of them split: step 410
+    // vs 407 us); a combine kernel merges them instead (mla_set_plan_override
+    // can force either).
+    pl.fused_combine = pl.P <= pl.batch && pl.M <= 128;
     const int mo = g_merge_override.load(std::memory_order_relaxed);
     if (mo >= 0) pl.fused_combine = mo == 1;
     // the 128-row kernel leaves every merge to the combine kernel
