@@ -351,12 +351,16 @@ FORCED_KERNEL = None
 
 
 def decode_kernel_name(fp8: bool, rows: int) -> str:
-    """The decode kernel a plan of `rows` query rows per sequence runs: the
-    library picks 16-row blocks below 64 rows and 64-row score/value blocks
-    from there, over either cache (--decode-kernel forces one)."""
-    kind = FORCED_KERNEL or ("rows16" if rows < 64 else "ws")
+    """The decode kernel a plan of `rows` query rows per sequence runs: over
+    the BF16 cache the library picks 16-row blocks below 64 rows and 64-row
+    score/value blocks from there; over the FP8 cache score/value blocks of
+    16, 32 or 64 rows (--decode-kernel forces one)."""
     if fp8:
-        return "mla_decode_rows16_fp8_kernel" if kind == "rows16" else "mla_decode_ws_kernel<4, true>"
+        kind = FORCED_KERNEL or "ws"
+        if kind == "rows16":
+            return "mla_decode_rows16_fp8_kernel"
+        return f"mla_decode_ws_kernel<{1 if rows <= 16 else 2 if rows <= 32 else 4}, true>"
+    kind = FORCED_KERNEL or ("rows16" if rows < 64 else "ws")
     return {"rows16": "mla_decode_rows16_kernel", "ws": "mla_decode_ws_kernel",
             "fw": "mla_decode_fw_kernel"}[kind]
 

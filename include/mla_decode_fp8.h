@@ -45,10 +45,10 @@ extern "C" {
  * mla_get_split_metadata_fp8 - the split plan for mla_decode_fwd_fp8.
  *
  * Same arguments, layout and semantics as mla_get_split_metadata. The FP8
- * decode uses 16-row blocks below 64 rows and 64-row blocks from 64 rows
- * on, like the BF16 decode, but never 16- or 32-row score/value blocks, so
- * the two calls' plans can differ; mla_metadata_bytes and
- * mla_workspace_bytes cover both.
+ * decode uses score/value blocks of 16, 32 or 64 rows (the smallest that
+ * holds a sequence's rows, 64 beyond), while the BF16 decode uses 16-row
+ * blocks below 64 rows, so the two calls' plans can differ (at 32 rows, for
+ * example); mla_metadata_bytes and mla_workspace_bytes cover both.
  */
 mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q, int s_q,
                                       int num_partitions, int32_t* metadata, size_t metadata_bytes,
@@ -62,13 +62,14 @@ mla_status mla_get_split_metadata_fp8(const int32_t* seqlens, int batch, int h_q
  *   metadata   from mla_get_split_metadata_fp8 (or NULL: computed in-call)
  *   (all other arguments as for mla_decode_fwd)
  *
- * Supported: h_q * s_q up to MLA_MAX_ROWS, as for mla_decode_fwd. Below 64
- * rows a 16-row kernel converts each wave's key stripe; from 64 rows a
- * 64-row kernel converts each half page once per workgroup into the BF16
- * layout its products read. A process whose kernel choice was forced to the
- * 16-row organisation (mla_set_plan_override) gets MLA_ERR_UNSUPPORTED above
- * 64 rows; the fused-wave override does not apply to FP8. Latent bytes of
- * used tokens must not be NaN patterns; scales must be finite.
+ * Supported: h_q * s_q up to MLA_MAX_ROWS, as for mla_decode_fwd. The
+ * score/value kernel keeps each half page in LDS as it is in memory and
+ * widens E4M3 to BF16 in registers as its two products read it. A process
+ * whose kernel choice was forced to the 16-row organisation
+ * (mla_set_plan_override: each wave converts its own key stripe into BF16
+ * first) gets MLA_ERR_UNSUPPORTED above 64 rows; the fused-wave override
+ * does not apply to FP8. Latent bytes of used tokens must not be NaN
+ * patterns; scales must be finite.
  */
 mla_status mla_decode_fwd_fp8(const void* q, const void* kv_cache, const int32_t* block_table,
                               int max_blocks_per_seq, const int32_t* seqlens, int batch, int s_q, int h_q,

@@ -169,8 +169,6 @@ __device__ __forceinline__ void block_barrier() {
 template <int kRT, bool kFp8>
 __global__ __launch_bounds__(WsShape<kRT>::kThreads) void mla_decode_ws_kernel(DecodeArgs a) {
     using Sh = WsShape<kRT>;
-    // the FP8 fill spreads a half page over eight waves: 64-row blocks only
-    static_assert(!kFp8 || kRT == 4, "FP8 cache: 64-row blocks");
     constexpr int kPB = kFp8 ? kF8PageBytes : kPageBytes;
     constexpr int kRows = Sh::kRows;
     constexpr int kSW = Sh::kScoreWaves;
@@ -869,8 +867,12 @@ hipError_t launch_decode_ws(const Plan& plan, const DecodeArgs& args, hipStream_
 }
 
 hipError_t launch_decode_ws_fp8(const Plan& plan, const DecodeArgs& args, hipStream_t stream) {
-    if (plan.tm != 64) return hipErrorInvalidValue;
-    return launch_ws<4, true>(plan, args, stream);
+    switch (plan.tm) {
+        case 16: return launch_ws<1, true>(plan, args, stream);
+        case 32: return launch_ws<2, true>(plan, args, stream);
+        case 64: return launch_ws<4, true>(plan, args, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace mla

@@ -229,13 +229,16 @@ def test_size_queries_cover_the_fp8_plan():
             w = lib.mla_workspace_bytes(batch, 128, s_q, 64)
             meta = 4 * (16 + 8 * 64 + 4 * batch + r * batch)      # P = 64
             assert m >= meta and w > 0
-    # under the score/value override the BF16 plan of 32 rows uses 32-row
-    # blocks (per-segment cost 3), the FP8 one 64-row blocks (cost 5)
+    # by default the BF16 plan of 32 rows has two 16-row blocks (R = 2), the
+    # FP8 one a 32-row score/value block (R = 1, per-segment cost 3); under
+    # the score/value override both take 32-row blocks and share the plan
+    lens = [300, 70, 129, 5000]
+    assert _host_plan(lens, 32, 1, 64)[8] == 2
+    assert _check_meta(_host_plan(lens, 32, 1, 64), 4, 32, 1, 64, fp8=1) == INVALID
     try:
         assert lib.mla_set_plan_override(1, -1) == OK
-        lens = [300, 70, 129, 5000]
         assert _host_plan(lens, 32, 1, 64)[3] == 3
-        assert _check_meta(_host_plan(lens, 32, 1, 64), 4, 32, 1, 64, fp8=1) == INVALID
+        assert _check_meta(_host_plan(lens, 32, 1, 64), 4, 32, 1, 64, fp8=1) == OK
     finally:
         lib.mla_set_plan_override(-1, -1)
 
@@ -292,8 +295,8 @@ def test_plan_header_check_on_host_plans():
         bad[0] ^= 1
         assert _check_meta(bad, 4, h_q, s_q, parts) == INVALID           # not a plan
         assert _check_meta(meta, 4, h_q, s_q, parts, nbytes=60) == TOO_SMALL
-    # by default the BF16 and FP8 calls cut rows alike (16-row blocks below 64
-    # rows, 64-row blocks from there) and share the plan
+    # by default the BF16 and FP8 calls cut 16 rows, and 64 rows and more,
+    # alike (one 16-row block; 64-row blocks) and share the plan
     assert _check_meta(_host_plan(lens, 64, 1, 64), 4, 64, 1, 64, fp8=1) == OK
     assert _check_meta(_host_plan(lens, 128, 2, 64), 4, 128, 2, 64, fp8=1) == OK
     assert _check_meta(_host_plan(lens, 16, 1, 64), 4, 16, 1, 64, fp8=1) == OK

@@ -72,6 +72,18 @@ def test_fp8_small_shapes(case):
     _check(inp, codes, rope, scales, f"small[{case}]", use_meta=case % 2 == 0)
 
 
+@pytest.mark.parametrize("case", [c for c, k in enumerate(FP8_CASES) if k[1] * k[2] <= 64])
+def test_fp8_small_shapes_16_row_organisation(case, plan_override):
+    """The 16-row FP8 organisation (each wave converts its own key stripe
+    into BF16 before both products), which the default plan no longer picks,
+    on every small case it supports (up to 64 rows)."""
+    plan_override(kernel="rows16")
+    seqlens, s_q, h_q, causal = FP8_CASES[case]
+    inp = make_inputs(seqlens, s_q, h_q, seed=300 + case, causal=causal)
+    codes, rope, scales = make_fp8_cache(inp, seed=400 + case)
+    _check(inp, codes, rope, scales, f"small-rows16[{case}]", use_meta=case % 2 == 0)
+
+
 @pytest.mark.parametrize("parts", [1, 8, 64, 512])
 @pytest.mark.parametrize("h_q", [16, 64, 128])
 def test_fp8_forced_splits(parts, h_q):
@@ -80,10 +92,11 @@ def test_fp8_forced_splits(parts, h_q):
     _check(inp, codes, rope, scales, f"splits h_q={h_q}", num_partitions=parts)
 
 
-@pytest.mark.parametrize("h_q", [16, 64])
-def test_fp8_poisoned_tails_are_ignored(h_q):
+@pytest.mark.parametrize("h_q,kernel", [(16, None), (64, None), (16, "rows16")])
+def test_fp8_poisoned_tails_are_ignored(h_q, kernel, plan_override):
     """Unused rows of last pages hold NaN latent bytes, NaN rotary values and
     NaN scales: the output must be bitwise what clean tails give."""
+    plan_override(kernel=kernel)
     inp = make_inputs([70, 5, 129, 64], 2, h_q, seed=320, causal=True)
     codes, rope, scales = make_fp8_cache(inp, seed=420)
     out0, lse0 = _check(inp, codes, rope, scales, "clean tails")
@@ -109,8 +122,8 @@ def test_fp8_combine_modes(mode, h_q, plan_override):
         _check(inp, codes, rope, scales, f"combine {mode}", num_partitions=parts)
 
 
-@pytest.mark.parametrize("h_q,s_q", [(16, 1), (64, 1), (128, 2)])
-def test_fp8_reference_restart_on_dominant_key(h_q, s_q):
+@pytest.mark.parametrize("h_q,s_q,kernel", [(16, 1, None), (64, 1, None), (128, 2, None), (16, 1, "rows16")])
+def test_fp8_reference_restart_on_dominant_key(h_q, s_q, kernel, plan_override):
     """Queries of 1.0 and, late in each sequence, a token whose latent values
     are all 448 * (0.5/448) = 0.5 and whose rotary values are 32: its score
     (512 * 0.5 + 64 * 32 = 2304 before the 1/24 scale, ~1.4e2 in log2 units)
@@ -120,6 +133,7 @@ def test_fp8_reference_restart_on_dominant_key(h_q, s_q):
     for (a BF16 output of magnitude 8 alone may round by 0.031), and must
     match the oracle."""
     import dataclasses
+    plan_override(kernel=kernel)
     inp = make_inputs([3000, 700, 150], s_q, h_q, seed=340)
     inp = dataclasses.replace(inp, q_bits=np.full_like(inp.q_bits, 0x3F80))
     codes, rope, scales = make_fp8_cache(inp, seed=440)

@@ -336,13 +336,13 @@ def test_mismatched_plan_writes_nan_lse_and_nothing_else(plan_override):
     cases = [  # (tag, plan h_q, plan partitions, call h_q, call partitions, fp8 call)
         ("partition count", 64, 128, 64, 64, False),
         ("row blocks", 64, 64, 128, 64, False),
-        # forced onto the score/value organisation, 32 rows take 32-row
-        # blocks over BF16 and 64-row blocks over FP8: the plans differ
+        # by default 32 rows take two 16-row blocks over BF16 and one 32-row
+        # score/value block over FP8: the plans differ
         ("BF16 plan into the FP8 call", 32, 64, 32, 64, True),
         ("16-row plan, other partition count", 16, 64, 16, 32, False),
     ]
     for tag, ph, pp, ch, cp, fp8 in cases:
-        plan_override(kernel="ws" if fp8 else None)
+        plan_override(kernel=None)
         meta = mla.get_split_metadata(sl, ph, 1, pp)
         host = meta.metadata.cpu().numpy()
         assert _lib.lib().mla_check_metadata_host(host.ctypes.data, host.nbytes, inp.batch, ch, 1, cp,
