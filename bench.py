@@ -802,8 +802,8 @@ def main():
                          % (", ".join(WORKLOADS), ", ".join(APPEND_WORKLOADS)))
     ap.add_argument("--op", default="decode",
                     choices=("decode", "decode_fp8", "kv_append", "kv_append_fp8", "absorb", "mha"),
-                    help="decode (the hot path; default), decode over an FP8 latent cache (workloads "
-                         "with h_q * s_q <= 64), the paged cache append, or the absorption products")
+                    help="decode (the hot path; default), decode over an FP8 latent cache, the paged "
+                         "cache append, the absorption products, or the MHA comparison decode")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU time for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--rotate-gib", type=float, default=1.0)
