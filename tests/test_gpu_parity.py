@@ -72,6 +72,21 @@ def test_small_shapes_fused_wave_forced(case, plan_override):
     _check(inp, tag=f"small-fw[{case}]")
 
 
+@pytest.mark.parametrize("h_q,parts", [(16, 8), (16, 16), (16, 24), (64, 8)])
+def test_combine_grid_over_partition_boundaries(h_q, parts, plan_override):
+    """More sequences than partition boundaries, merged by the combine
+    kernel: its grid follows the boundaries (each split sequence merged once,
+    by the group of its first cut) and a tail of blocks writes the empty
+    sequences, here five of 37."""
+    plan_override(merge="kernel")
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 700, size=37)]
+    for e in (0, 5, 17, 30, 36):
+        lens[e] = 0
+    inp = make_inputs(lens, 1, h_q, seed=50 + parts)
+    _check(inp, num_partitions=parts, tag=f"boundary combine h_q={h_q} parts={parts}")
+
+
 @pytest.mark.parametrize("parts", [1, 8, 24, 64, 512])
 @pytest.mark.parametrize("shape", [(16, 1, False), (64, 1, False), (128, 2, True)])
 def test_forced_splits(parts, shape):
