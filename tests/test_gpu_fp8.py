@@ -15,10 +15,28 @@ from workloads import FP8_PAGE_BYTES, make_fp8_cache, make_inputs, make_workload
 
 pytestmark = pytest.mark.gpu
 
+# the organisation --decode-kernel forces for the whole run (None: default)
+_forced_kernel = None
+
+
+@pytest.fixture(autouse=True)
+def _note_forced_kernel(request):
+    global _forced_kernel
+    _forced_kernel = request.config.getoption("--decode-kernel")
+    yield
+
+
+def _skip_beyond_16_row_limit(rows):
+    """A run forced onto the 16-row organisation cannot decode FP8 query
+    blocks above 64 rows (the call returns MLA_ERR_UNSUPPORTED by design)."""
+    if _forced_kernel == "rows16" and rows > 64:
+        pytest.skip("the forced 16-row FP8 organisation stops at 64 rows")
+
 
 def _run(inp, codes, rope, scales, num_partitions=0, use_meta=True):
     import torch
     import mla_paged_kv_02_amd as mla
+    _skip_beyond_16_row_limit(inp.h_q * inp.s_q)
     q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).cuda()
     pages = torch.from_numpy(pack_fp8_pages(codes, rope, scales)).cuda()
     bt = torch.from_numpy(inp.block_table).cuda()

@@ -42,7 +42,17 @@ def _call(inp, noalloc, use_meta, parts=0):
     return out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()
 
 
+# MLA_NOALLOC_SCRATCH_BYTES in include/mla_decode.h
+NOALLOC_SCRATCH_BYTES = 72 << 20
+
+
 def _compare(inp, tag, use_meta, parts=0):
+    from mla_paged_kv_02_amd import _lib
+    need = _lib.lib().mla_workspace_bytes(inp.batch, inp.h_q, inp.s_q, parts)
+    if need > NOALLOC_SCRATCH_BYTES:
+        # only under a forced organisation (--decode-kernel fw: 128-row
+        # blocks take more partial slots); every default plan here fits
+        pytest.skip(f"{tag}: workspace {need} B beyond the allocation-free scratch under this plan choice")
     log(f"[case] noalloc {tag}: B={inp.batch} s_q={inp.s_q} h_q={inp.h_q} meta={use_meta} parts={parts}")
     a = _call(inp, False, use_meta, parts)
     b = _call(inp, True, use_meta, parts)
