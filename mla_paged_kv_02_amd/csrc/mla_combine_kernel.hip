@@ -119,16 +119,28 @@ __global__ __launch_bounds__(64 * (kWPI > 4 ? kWPI : 4)) void mla_combine_kernel
         }
     }
 
-    // combined lse (every wave of the item computes it; a few loads per lane)
-    float m = -INFINITY;
-    for (int s = lane; s < cnt; s += 64) m = fmaxf(m, lp[s]);
+    // combined lse (every wave of the item computes it). A wave that owns
+    // all of an item's partials (one wave per item, at most one group of
+    // them) already holds every lse_s in wt[]: no loads, no lane exchange.
+    // Otherwise the lanes load the lse_s a few apiece and reduce.
+    float m = -INFINITY, tot = 0.f, m_use = 0.f;
+    if (kWPI == 1 && cnt <= kCombineUnroll) {
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, wave_xor(m, d));
-    const float m_use = (m == -INFINITY) ? 0.f : m;
-    float tot = 0.f;
-    for (int s = lane; s < cnt; s += 64) tot += __builtin_amdgcn_exp2f((lp[s] - m_use) * kLog2e);
+        for (int u = 0; u < kCombineUnroll; ++u)
+            if (u < cnt) m = fmaxf(m, wt[u]);
+        m_use = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) tot += wave_xor(tot, d);
+        for (int u = 0; u < kCombineUnroll; ++u)
+            if (u < cnt) tot += __builtin_amdgcn_exp2f((wt[u] - m_use) * kLog2e);
+    } else {
+        for (int s = lane; s < cnt; s += 64) m = fmaxf(m, lp[s]);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) m = fmaxf(m, wave_xor(m, d));
+        m_use = (m == -INFINITY) ? 0.f : m;
+        for (int s = lane; s < cnt; s += 64) tot += __builtin_amdgcn_exp2f((lp[s] - m_use) * kLog2e);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) tot += wave_xor(tot, d);
+    }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
