@@ -148,18 +148,25 @@ __global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(App
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * (kAppendF8Threads / 64) + (threadIdx.x >> 6);   // token of this wave
     if (t >= a.tokens) return;
-    const int b = t / a.s_new;
-    const int i = t - b * a.s_new;
-    const int p = a.seqlens[b] - a.s_new + i;
-    if (p < 0) return;
-    const int blk = p >> 6;
-    const int page = blk < a.max_blocks ? a.block_table[(size_t)b * a.max_blocks + blk] : -1;
-    if (page < 0 || page >= a.num_pages) {
-        if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);
-        return;
-    }
+    // The row's loads go out first, with the sequence length beside them; the
+    // table entry's load, which needs the length, then flies while the wave
+    // quantises the row. So a wave waits two memory latencies before its
+    // stores, not three (length, entry, row) plus the arithmetic. Indices are
+    // clamped into their buffers and checked only before the stores.
     const uint16_t* row = a.src + (size_t)t * kHeadDim;
     const u32x4 lat = *reinterpret_cast<const u32x4*>(row + 8 * lane);
+    u32x4 rope = {0u, 0u, 0u, 0u};
+    if (lane < 8) rope = *reinterpret_cast<const u32x4*>(row + 512 + 8 * lane);
+    const int b = t / a.s_new;
+    const int i = t - b * a.s_new;
+    const int len = a.seqlens[b];
+    // (the scheduler would otherwise start on the row, and so wait for it,
+    // before these loads are issued)
+    __builtin_amdgcn_sched_barrier(0);
+    const int p = len - a.s_new + i;
+    const int blk = max(p, 0) >> 6;
+    const int page = a.block_table[(size_t)b * a.max_blocks + min(blk, a.max_blocks - 1)];
+    __builtin_amdgcn_sched_barrier(0);
     float x[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -177,13 +184,16 @@ __global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(App
     for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k], scale) << (8 * k);
 #pragma unroll
     for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k], scale) << (8 * k);
+    if (p < 0) return;
+    if (blk >= a.max_blocks || page < 0 || page >= a.num_pages) {
+        if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);
+        return;
+    }
     const int slot = p & (kPageRows - 1);
     uint8_t* grp = a.pages + (size_t)page * MLA_FP8_PAGE_BYTES + (slot >> 4) * (MLA_FP8_PAGE_BYTES / 4);
     const int r = slot & 15;
     *reinterpret_cast<uint2*>(grp + r * 512 + 8 * lane) = uint2{lo, hi};
-    if (lane < 8)
-        *reinterpret_cast<u32x4*>(grp + 8192 + r * 128 + 16 * lane) =
-            *reinterpret_cast<const u32x4*>(row + 512 + 8 * lane);
+    if (lane < 8) *reinterpret_cast<u32x4*>(grp + 8192 + r * 128 + 16 * lane) = rope;
     if (lane == 0) *reinterpret_cast<float*>(grp + 10240 + 4 * r) = scale;
 }
 
