@@ -87,17 +87,16 @@ __global__ __launch_bounds__(kAppendThreads) void mla_kv_append_kernel(AppendArg
 // magnitude comes from a wave reduction and scale = amax / 448 is an FP32
 // division (correctly rounded: the stored scale is the FP32 number nearest
 // amax / 448). Each code is the E4M3 value nearest the exact quotient
-// |x| / scale, ties to the even mantissa: y = fl32(x / scale) is rounded to
-// E4M3 in integer arithmetic (magnitudes at or past 448 saturate to 448;
-// below 2^-6 the code is rint(|y| * 2^9), subnormal steps of 2^-9; above,
-// |y| * 2^(3 - e) lies in [8, 16) for e = floor(log2 |y|) and its rounding
-// gives the mantissa, a carry to 16 moving to the next binade by itself:
-// code = 8 (e + 7) + r - 8). Only where y lands exactly on a midpoint can
-// the exact quotient lie on the other side of it than y suggests; there
-// the sign of the residual |x| - |y| * scale, computed exactly by one FMA,
-// says which side (zero: an exact midpoint, ties to even). Rounding is
-// monotonic, so a y off a midpoint is on the same side as the exact
-// quotient. The sign bit is x's.
+// |x| / scale, ties to the even mantissa: y = |x| * fl32(1 / scale), within
+// a relative 2^-23 of the quotient, is rounded to E4M3 in integer arithmetic
+// (magnitudes at or past 448 saturate to 448; below 2^-6 the code is the
+// rounding of y * 2^9, subnormal steps of 2^-9; above, y * 2^(3 - e) lies in
+// [8, 16) for e = floor(log2 y) and its rounding gives the mantissa, a carry
+// to 16 moving to the next binade by itself: code = 8 (e + 7) + r - 8). A y
+// whose grid position is within 2^-18 of a midpoint may sit on the other
+// side of it than the exact quotient; there the sign of the exact residual
+// at the midpoint decides (round_grid). Where y crosses a binade edge
+// instead, both sides give the same code. The sign bit is x's.
 constexpr int kAppendF8Threads = 256;   // four tokens per workgroup
 
 struct AppendF8Args {
@@ -109,35 +108,43 @@ struct AppendF8Args {
     int batch, s_new, max_blocks, num_pages, tokens;
 };
 
-// t = |y| in grid-step units (the mantissa position, or |y| * 2^9 below
-// 2^-6): rounded to nearest, a half-way t decided by the residual's sign.
-__device__ __forceinline__ float round_grid(float t, float resid) {
-    const float fl = floorf(t);
-    if (t - fl != 0.5f) return rintf(t);
+// Round t = q / step (q = |x| / scale in grid-step units: the mantissa
+// position, or q * 2^9 below 2^-6) to the nearest integer, where tq is t
+// computed from a = |x| * fl32(1 / scale), within a relative 2^-23 of t
+// (two roundings of 2^-24), so |tq - t| <= 16 * 2^-23 = 2^-19. A tq more
+// than 2^-18 from the midpoint fl + 1/2 of its unit interval is on the same
+// side of it as t, and rint decides. Closer, the sign of the exact residual
+// |x| - (fl + 1/2) * step * scale decides (one FMA: the midpoint has at most
+// five significant bits, so the product is exact and the single rounding
+// keeps the sign; zero is an exact tie, to the even integer). `up` scales
+// both operands by 2^64 for |x| < 2^-60, so the residual never underflows.
+__device__ __forceinline__ float round_grid(float tq, float step, float ax, float scale, float up) {
+    const float fl = floorf(tq);
+    const float d = tq - fl - 0.5f;   // exact
+    if (fabsf(d) > 0x1p-18f) return rintf(tq);
+    const float mid = (fl + 0.5f) * step;   // exact
+    const float resid = fmaf(-(mid * up), scale, ax * up);
     if (resid > 0.f) return fl + 1.f;
     if (resid < 0.f) return fl;
-    return rintf(t);   // an exact midpoint: even
+    return ((int)fl & 1) == 0 ? fl : fl + 1.f;
 }
 
-__device__ __forceinline__ uint32_t e4m3_code(float x, float scale) {
+// E4M3 code of x, the value nearest the exact quotient |x| / scale (ties to
+// the even mantissa); rinv = fl32(1 / (scale * up_s)), where up_s = 2^64 for
+// a scale below 2^-64 (whose reciprocal would overflow) and 1 otherwise.
+__device__ __forceinline__ uint32_t e4m3_code(float x, float scale, float rinv, float up_s) {
     const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-    const float a = fabsf(x / scale);
     const float ax = fabsf(x);
-    // |x| - a * scale exactly: a at a midpoint has at most five significant
-    // bits and the product at most 29, so one FMA rounds the exact residual
-    // only where it would fall below the FP32 range; for |x| < 2^-60 both
-    // operands are first scaled by 2^64 (exact) so that it never does
+    const float a = (ax * up_s) * rinv;   // the scaling by up_s is exact
     const float up = ax < 0x1p-60f ? 0x1p64f : 1.f;
     uint32_t mag;
     if (!(a < 448.f)) {
-        mag = 0x7Eu;
+        mag = 0x7Eu;   // at or past the largest code (and NaN)
     } else if (a < 0x1p-6f) {
-        const float t = a * 0x1p9f;
-        mag = (uint32_t)round_grid(t, t - floorf(t) == 0.5f ? fmaf(-a, scale * up, ax * up) : 0.f);
+        mag = (uint32_t)round_grid(a * 0x1p9f, 0x1p-9f, ax, scale, up);
     } else {
         const int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;    // -6 .. 8
-        const float t = ldexpf(a, 3 - e);                                 // 8 .. 16
-        const float r = round_grid(t, t - floorf(t) == 0.5f ? fmaf(-a, scale * up, ax * up) : 0.f);
+        const float r = round_grid(ldexpf(a, 3 - e), ldexpf(1.f, e - 3), ax, scale, up);   // 8 .. 16
         mag = (uint32_t)(8 * (e + 7) + (int)r - 8);
         mag = mag > 0x7Eu ? 0x7Eu : mag;
     }
@@ -179,11 +186,13 @@ __global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(App
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
+    const float up_s = scale < 0x1p-64f ? 0x1p64f : 1.f;
+    const float rinv = 1.f / (scale * up_s);
     uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k], scale) << (8 * k);
+    for (int k = 0; k < 4; ++k) lo |= e4m3_code(x[k], scale, rinv, up_s) << (8 * k);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k], scale) << (8 * k);
+    for (int k = 0; k < 4; ++k) hi |= e4m3_code(x[4 + k], scale, rinv, up_s) << (8 * k);
     if (p < 0) return;
     if (blk >= a.max_blocks || page < 0 || page >= a.num_pages) {
         if (lane == 0 && a.skipped) atomicAdd(a.skipped, 1);

@@ -227,6 +227,12 @@ def test_fp8_append_holes_and_extremes():
         nb[0, 1, :512] = 0x0001
         nb[0, 1, 7] = 0x7F00
         nb[0, 2, :512] = 0x8000
+        if nb.shape[1] > 4:
+            # rows of only tiny magnitudes: BF16 subnormals (the scale, amax / 448,
+            # is then an FP32 subnormal) and the smallest normal binades, both signs
+            i = np.arange(512)
+            nb[0, 3, :512] = ((i % 127) + 1) | ((i % 3 == 0) << 15)
+            nb[0, 4, :512] = ((1 + i % 8) << 7) | (i * 37 % 128) | ((i % 5 == 0) << 15)
         _append_fp8_case(type(inp)(inp.seqlens, inp.block_table, inp.kv_bits, nb), f"holes[{k}]")
 
 
