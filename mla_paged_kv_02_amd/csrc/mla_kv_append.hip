@@ -129,6 +129,27 @@ __device__ __forceinline__ float round_grid(float tq, float step, float ax, floa
     return ((int)fl & 1) == 0 ? fl : fl + 1.f;
 }
 
+// Maximum over the 64 lanes, in every lane: DPP within each row of 16 (quad
+// swaps, then the half-row and row mirrors pair lanes i and 7 - i, i and
+// 15 - i), then across rows with the lane-swap VALU ops; no LDS round trip.
+__device__ __forceinline__ float dpp_max(float v, int ctrl_sel) {
+    int m;
+    switch (ctrl_sel) {
+        case 0: m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false); break;   // quad [1,0,3,2]
+        case 1: m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false); break;   // quad [2,3,0,1]
+        case 2: m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+        default: m = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return fmaxf(v, __int_as_float(m));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = dpp_max(v, 0);
+    v = dpp_max(v, 1);
+    v = dpp_max(v, 2);
+    v = dpp_max(v, 3);
+    return max_over_kgroups(v);
+}
+
 // E4M3 code of x, the value nearest the exact quotient |x| / scale (ties to
 // the even mantissa); rinv = fl32(1 / (scale * up_s)), where up_s = 2^64 for
 // a scale below 2^-64 (whose reciprocal would overflow) and 1 otherwise.
@@ -183,8 +204,7 @@ __global__ __launch_bounds__(kAppendF8Threads) void mla_kv_append_fp8_kernel(App
     float amax = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    amax = wave_max(amax);
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
     const float up_s = scale < 0x1p-64f ? 0x1p64f : 1.f;
     const float rinv = 1.f / (scale * up_s);
