@@ -51,7 +51,7 @@ def _check_product(got_bits, ref, w, x, k, what):
 
 
 @pytest.mark.parametrize("tokens,heads,d_nope", [(1, 1, 32), (5, 3, 96), (70, 16, 128), (130, 128, 128),
-                                                 (33, 8, 512), (64, 2, 64)])
+                                                 (9, 3, 128), (33, 8, 512), (64, 2, 64)])
 def test_absorb_q_matches_oracle(tokens, heads, d_nope):
     import torch
     import mla_paged_kv_02_amd as mla
