@@ -42,7 +42,8 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # kernels out, so that changing one op does not void another's counter figures.
 OP_SOURCES = {"kv_append": ("mla_kv_append.hip", "mla_common.h"),
               "absorb": ("mla_absorb.hip", "mla_common.h"),
-              "mha": ("mla_mha_decode.hip", "mla_common.h")}
+              "mha": ("mla_mha_decode.hip", "mla_common.h"),
+              "check": ("mla_check.hip",)}
 
 
 def kernel_digest(op: str = "decode") -> str:

@@ -195,6 +195,37 @@ mla_status mla_decode_fwd(const void* q, const void* kv_cache, const int32_t* bl
                           size_t workspace_bytes, void* out, float* lse, void* stream);
 
 /*
+ * mla_check_decode_inputs - checks on the device the preconditions of
+ * mla_decode_fwd (and of the FP8 and allocation-free variants) that the host
+ * cannot see: the paged cache of the "FlashMLA Overview" page, variable-length
+ * sequences in 64-token blocks looked up through a per-sequence block table.
+ * Counts into *violations (written, not added to) every way the inputs break
+ * them: a sequence length below 0 or above 64 * max_blocks_per_seq (counted
+ * once; that sequence's entries are then not checked), and every entry
+ * block_table[b][n] with n < ceil(seqlens[b] / 64) outside [0, num_pages).
+ * Entries past a sequence's last page are never read by the decode and are
+ * not checked. 0 means the decode's device preconditions hold.
+ *
+ *   block_table          device int32 [batch][max_blocks_per_seq], 4-byte aligned
+ *   max_blocks_per_seq   row stride of block_table, >= 1
+ *   seqlens              device int32 [batch], 4-byte aligned
+ *   batch                >= 1
+ *   num_pages            number of physical pages of the cache, >= 1
+ *   violations           device int32, 4-byte aligned (written)
+ *   stream               hipStream_t
+ *
+ * Enqueues one small single-workgroup kernel on `stream` and returns without
+ * waiting; the caller reads *violations back after the stream reaches it.
+ * It reads the used part of the whole table, so it is meant for debugging
+ * and tests, not for every decode step. Returns MLA_OK;
+ * MLA_ERR_INVALID_ARG for a NULL pointer or a size below 1;
+ * MLA_ERR_UNSUPPORTED when batch * max_blocks_per_seq exceeds 2^31 - 1;
+ * MLA_ERR_MISALIGNED; MLA_ERR_HIP if the launch fails.
+ */
+mla_status mla_check_decode_inputs(const int32_t* block_table, int max_blocks_per_seq, const int32_t* seqlens,
+                                   int batch, int num_pages, int32_t* violations, void* stream);
+
+/*
  * mla_decode_fwd_noalloc - mla_decode_fwd for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments without

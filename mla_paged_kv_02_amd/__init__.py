@@ -199,6 +199,30 @@ def _decode(fn, name, q, kv_cache, block_table, seqlens, softmax_scale, causal, 
     return out, lse
 
 
+def check_decode_inputs(block_table: torch.Tensor, seqlens: torch.Tensor, num_pages: int,
+                        violations: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Count on the device the decode-precondition violations of a block
+    table and lengths (mla_check_decode_inputs): lengths outside
+    [0, 64 * max_blocks] and table entries the decode would read outside
+    [0, num_pages). Returns the int32 scalar tensor the count is written to
+    (``violations`` if given), on the stream; 0 means the inputs are valid."""
+    dev = block_table.device
+    _require(block_table, "block_table", torch.int32, device=dev, ndim=2)
+    _require(seqlens, "seqlens", torch.int32, device=dev, ndim=1)
+    if block_table.shape[0] != seqlens.shape[0]:
+        raise ValueError("block_table and seqlens must have one row per sequence")
+    if violations is None:
+        violations = torch.empty((), dtype=torch.int32, device=dev)
+    else:
+        _require(violations, "violations", torch.int32, device=dev)
+        if violations.numel() != 1:
+            raise ValueError("violations must hold one int32")
+    check(lib().mla_check_decode_inputs(block_table.data_ptr(), block_table.shape[1], seqlens.data_ptr(),
+                                        seqlens.shape[0], int(num_pages), violations.data_ptr(), _stream_ptr(dev)),
+          "mla_check_decode_inputs")
+    return violations
+
+
 def kv_append(new_rows: torch.Tensor, seqlens: torch.Tensor, block_table: torch.Tensor,
               kv_cache: torch.Tensor, skipped: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Write the new tokens' cache rows into the paged cache (mla_kv_append).

@@ -47,6 +47,7 @@ SIGNATURES = {
     "mla_mha_decode_fwd": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                     _c_int, _c_float, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "mla_set_plan_override": (_c_int, [_c_int, _c_int]),
+    "mla_check_decode_inputs": (_c_int, [_c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_ptr, _c_ptr]),
     "mla_decode_fwd_noalloc": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_ptr, _c_int, _c_int, _c_int, _c_int,
                                         _c_float, _c_int, _c_ptr, _c_int, _c_ptr, _c_ptr, _c_ptr]),
     "mla_timing_enable": (_c_int, [_c_int]),

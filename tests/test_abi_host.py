@@ -140,6 +140,24 @@ def test_append_argument_checks(kw, status):
     assert _append(**kw) == status
 
 
+def _check_inputs(**kw):
+    args = dict(bt=FAKE, maxb=4, seqlens=FAKE, batch=2, pages=8, out=FAKE, stream=None)
+    args.update(kw)
+    return _lib.lib().mla_check_decode_inputs(args["bt"], args["maxb"], args["seqlens"], args["batch"],
+                                              args["pages"], args["out"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bt=None), INVALID), (dict(seqlens=None), INVALID), (dict(out=None), INVALID),
+    (dict(batch=0), INVALID), (dict(maxb=0), INVALID), (dict(pages=0), INVALID),
+    (dict(batch=1 << 16, maxb=1 << 16), UNSUPPORTED),
+    (dict(bt=FAKE + 2), MISALIGNED), (dict(seqlens=FAKE + 1), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED),
+])
+def test_check_decode_inputs_argument_checks(kw, status):
+    """Rejected on the host, before any HIP call."""
+    assert _check_inputs(**kw) == status
+
+
 def _absorb_q(**kw):
     args = dict(qn=FAKE, qr=FAKE, w=FAKE, tokens=4, h=2, dn=128, out=FAKE, stream=None)
     args.update(kw)
