@@ -1,0 +1,86 @@
+"""Guard bands around every buffer the decode writes: out, lse and the
+workspace are views into the middle of larger buffers whose margins hold a
+known pattern, and after the call the margins must be bit for bit unchanged
+(no store outside its buffer, whatever the organisation, split count or
+cache format). The results inside are compared with the oracle as well."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import log, score
+from workloads import make_fp8_cache, make_inputs, pack_fp8_pages
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096   # bytes on each side (keeps every view 256-byte aligned)
+
+CASES = [
+    # (seqlens, s_q, h_q, causal, partitions, forced organisation, fp8)
+    ([37, 100, 0, 300], 1, 16, False, 0, None, False),
+    ([37, 100, 0, 300], 1, 16, False, 24, None, False),
+    ([130, 70, 3], 1, 80, False, 0, None, False),
+    ([200, 64, 9], 2, 128, True, 8, None, False),
+    ([300, 5], 1, 64, False, 32, None, False),
+    ([150, 65], 1, 128, False, 16, "fw", False),
+    ([90, 45, 1], 1, 24, False, 8, "ws", False),
+    ([37, 100, 0, 300], 1, 16, False, 8, None, True),
+    ([200, 64, 9], 2, 128, True, 8, None, True),
+]
+
+
+def _guarded(nbytes, fill_byte, device):
+    """(full uint8 buffer, view of nbytes in its middle)."""
+    full = torch.full((GUARD + nbytes + GUARD,), fill_byte, dtype=torch.uint8, device=device)
+    return full, full[GUARD:GUARD + nbytes]
+
+
+def _margins_intact(full, nbytes, fill_byte):
+    host = full.cpu().numpy()
+    return bool((host[:GUARD] == fill_byte).all() and (host[GUARD + nbytes:] == fill_byte).all())
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_decode_writes_only_its_buffers(case, plan_override):
+    import mla_paged_kv_02_amd as mla
+    seqlens, s_q, h_q, causal, parts, kernel, fp8 = CASES[case]
+    log(f"[case] guards {CASES[case]}")
+    if kernel is not None:
+        plan_override(kernel=kernel)
+    dev = torch.device("cuda:0")
+    inp = make_inputs(seqlens, s_q=s_q, h_q=h_q, seed=900 + case, causal=causal)
+    q = torch.from_numpy(inp.q_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    bt = torch.from_numpy(inp.block_table).to(dev)
+    sl = torch.from_numpy(inp.seqlens).to(dev)
+    B, M = inp.batch, s_q * h_q
+    out_bytes, lse_bytes = B * M * 512 * 2, B * M * 4
+    ws_bytes = mla.workspace_bytes(B, h_q, s_q, parts)
+    out_full, out_v = _guarded(out_bytes, 0xA5, dev)
+    lse_full, lse_v = _guarded(lse_bytes, 0x5A, dev)
+    ws_full, ws_v = _guarded(ws_bytes, 0xC3, dev)
+    out = out_v.view(torch.bfloat16).view(B, s_q, h_q, 512)
+    lse = lse_v.view(torch.float32).view(B, s_q, h_q)
+    if fp8:
+        codes, rope, scales = make_fp8_cache(inp, seed=950 + case)
+        pages = torch.from_numpy(pack_fp8_pages(codes, rope, scales)).to(dev)
+        meta = mla.get_split_metadata(sl, h_q, s_q, parts, fp8=True)
+        mla.decode_fwd_fp8(q, pages, bt, sl, inp.scale, causal, meta=meta, out=out, lse=lse, workspace=ws_v)
+    else:
+        kv = torch.from_numpy(inp.kv_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        meta = mla.get_split_metadata(sl, h_q, s_q, parts)
+        mla.decode_fwd(q, kv, bt, sl, inp.scale, causal, meta=meta, out=out, lse=lse, workspace=ws_v)
+    torch.cuda.synchronize()
+    assert _margins_intact(out_full, out_bytes, 0xA5), "a store landed outside out"
+    assert _margins_intact(lse_full, lse_bytes, 0x5A), "a store landed outside lse"
+    assert _margins_intact(ws_full, ws_bytes, 0xC3), "a store landed outside the workspace"
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    if fp8:
+        ref_out, ref_lse = oracle.mla_decode_fp8_ref(inp.q_bits, codes, rope, scales, inp.block_table,
+                                                     inp.seqlens, inp.scale, causal)
+    else:
+        ref_out, ref_lse = oracle.mla_decode_ref(inp.q_bits, inp.kv_bits, inp.block_table, inp.seqlens,
+                                                 inp.scale, causal)
+    s = score(got, lse.cpu().numpy(), ref_out, ref_lse)
+    log(f"       {s}")
+    assert s.ok(), str(s)
