@@ -104,6 +104,22 @@ def build(verbose: bool = False, extra_flags=(), hostsan: bool = False, out_path
     return out_path
 
 
+# Test-only probe library (tests/tile_probe): the decode kernels' building
+# blocks run one at a time, for the tile tests.
+PROBE_SRC = os.path.join(os.path.dirname(HERE), "tests", "tile_probe", "tile_probe.hip")
+PROBE_LIB_PATH = os.path.join(os.path.dirname(PROBE_SRC), "libtile_probe.so")
+
+
+def build_probe() -> str:
+    tmp_lib = PROBE_LIB_PATH + ".tmp"
+    cmd = [HIPCC, "-x", "hip", "-shared", "-fPIC", PROBE_SRC, "-o", tmp_lib, *COMMON_FLAGS]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the tile probe:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp_lib, PROBE_LIB_PATH)
+    return PROBE_LIB_PATH
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv, hostsan="--hostsan" in sys.argv)
     print(path)
