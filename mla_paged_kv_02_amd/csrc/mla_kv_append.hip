@@ -120,7 +120,7 @@ struct AppendF8Args {
 // both operands by 2^64 for |x| < 2^-60, so the residual never underflows.
 __device__ __forceinline__ float round_grid(float tq, float step, float ax, float scale, float up) {
     const float fl = floorf(tq);
-    const float d = tq - fl - 0.5f;   // exact
+    const float d = tq - fl - 0.5f;   // exact wherever |d| is small
     if (fabsf(d) > 0x1p-18f) return rintf(tq);
     const float mid = (fl + 0.5f) * step;   // exact
     const float resid = fmaf(-(mid * up), scale, ax * up);
