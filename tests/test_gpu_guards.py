@@ -42,9 +42,11 @@ def _margins_intact(full, nbytes, fill_byte):
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
-def test_decode_writes_only_its_buffers(case, plan_override):
+def test_decode_writes_only_its_buffers(case, plan_override, request):
     import mla_paged_kv_02_amd as mla
     seqlens, s_q, h_q, causal, parts, kernel, fp8 = CASES[case]
+    if fp8 and request.config.getoption("--decode-kernel") == "rows16" and s_q * h_q > 64:
+        pytest.skip("the forced 16-row FP8 organisation stops at 64 rows")
     log(f"[case] guards {CASES[case]}")
     if kernel is not None:
         plan_override(kernel=kernel)
