@@ -111,34 +111,48 @@ __global__ __launch_bounds__(kSchedThreads) void mla_split_meta_kernel(const int
     }
     __syncthreads();
 
-    // partition boundaries: boundary_at, searching the LDS copy of the
-    // starts when there is one
-    auto bound = [&](int64_t x, int32_t* b_out, int32_t* n_out) {
-        if (!in_lds) {
-            boundary_at(x, seq + 3, 4, batch, total, cseg, b_out, n_out);
-            return;
-        }
-        if (x >= total) {
-            *b_out = batch;
-            *n_out = 0;
-            return;
-        }
-        int lo = 0, hi = batch - 1;   // largest b with s_start[b] <= x
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_start[mid] <= x) lo = mid; else hi = mid - 1;
-        }
-        const int64_t off = x - s_start[lo] - cseg;
-        *b_out = lo;
-        *n_out = off < 0 ? 0 : (int32_t)off;
-    };
+    // partition boundaries (boundary_at). With the starts in LDS both
+    // boundaries of a partition are found together by radix-4 lifting for the
+    // largest b with start[b] <= x: per level three probes per boundary, the
+    // six LDS reads issued at once (indexes clamped into the batch, the test
+    // keeps j < batch), one round trip per level instead of two chains of
+    // binary-search steps. Larger batches search the copy in the metadata.
+    int s4 = 1;   // largest power of 4 <= batch - 1 (1 for batch <= 4)
+    while ((int64_t)s4 * 4 <= batch - 1) s4 *= 4;
     for (int p = tid; p < P; p += kSchedThreads) {
         int32_t* e = meta + kMetaHeader + kPartInts * p;
         if (p < pa) {
             // partition_start(p) = floor(p * total / pa)
             int32_t v[4];
-            bound(floor_div((int64_t)p * total, pa), &v[0], &v[1]);
-            bound(floor_div((int64_t)(p + 1) * total, pa), &v[2], &v[3]);
+            const int64_t x0 = floor_div((int64_t)p * total, pa);
+            const int64_t x1 = floor_div((int64_t)(p + 1) * total, pa);
+            if (in_lds) {
+                // s_start[0] = 0 <= x, and the probes reach 4 * s4 - 1 >= batch - 1
+                int lo0 = 0, lo1 = 0;
+                for (int st = s4; st > 0; st >>= 2) {
+                    int c0 = 0, c1 = 0;
+#pragma unroll
+                    for (int i = 1; i <= 3; ++i) {
+                        const int j0 = lo0 + i * st, j1 = lo1 + i * st;
+                        const int32_t a0 = s_start[j0 < batch ? j0 : batch - 1];
+                        const int32_t a1 = s_start[j1 < batch ? j1 : batch - 1];
+                        c0 += (j0 < batch && a0 <= x0) ? 1 : 0;
+                        c1 += (j1 < batch && a1 <= x1) ? 1 : 0;
+                    }
+                    lo0 += c0 * st;
+                    lo1 += c1 * st;
+                }
+                // x0 < total; x1 = total for the last active partition
+                const int64_t off0 = x0 - s_start[lo0] - cseg;
+                const int64_t off1 = x1 - s_start[lo1] - cseg;
+                v[0] = lo0;
+                v[1] = off0 < 0 ? 0 : (int32_t)off0;
+                v[2] = x1 >= total ? batch : lo1;
+                v[3] = x1 >= total ? 0 : (off1 < 0 ? 0 : (int32_t)off1);
+            } else {
+                boundary_at(x0, seq + 3, 4, batch, total, cseg, &v[0], &v[1]);
+                boundary_at(x1, seq + 3, 4, batch, total, cseg, &v[2], &v[3]);
+            }
             e[0] = v[0]; e[1] = v[1]; e[2] = v[2]; e[3] = v[3];
             e[4] = v[0] < batch ? (in_lds ? s_len[v[0]] : seqlens[v[0]]) : 0;
         } else {
