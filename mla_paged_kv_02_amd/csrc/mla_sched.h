@@ -6,9 +6,11 @@
 // a fresh segment), then one unit per page. Empty sequences take no room.
 // Partition p owns the cost interval [p*W, (p+1)*W), W = ceil(total / P),
 // and therefore a contiguous run of pages that may start or end inside a
-// sequence. Each boundary is found independently (binary search over the
-// sequence prefix sums), so the device builds the plan in parallel and the
-// host builds the identical plan sequentially from the same functions.
+// sequence. Each boundary is found independently (the last sequence whose
+// prefix sum is at most the boundary's position), so the device builds the
+// plan in parallel and the host builds the identical plan sequentially from
+// the same functions; the device kernel runs that search as radix-4 lifting
+// over a copy of the prefix sums in LDS, which finds the same sequence.
 //
 // Why: decode has one new token per sequence, so parallelising over batch
 // alone leaves most compute units idle when batch is small and contexts are
