@@ -165,6 +165,29 @@ def test_device_metadata_matches_host():
         assert np.array_equal(meta.metadata.cpu().numpy(), host), f"device metadata differs, batch={batch}"
 
 
+@pytest.mark.parametrize("batch", [1, 2, 4, 5, 16, 17, 64, 65, 256, 257, 1024, 1025, 4096, 4097, 8192])
+def test_device_metadata_matches_host_at_search_depths(batch):
+    """Device plan = host plan at every batch size where the device's search
+    of the cost-line starts in LDS changes depth (radix 4: 1, 4, 16, ...
+    sequences per probe step) up to the largest batch it keeps in LDS, with a
+    quarter of the sequences empty (equal starts) and partition counts below,
+    at and above the number of pages."""
+    import torch
+    import mla_paged_kv_02_amd as mla
+    rng = np.random.default_rng(1000 + batch)
+    seqlens = rng.integers(1, 3000, size=batch).astype(np.int32)
+    seqlens[rng.random(batch) < 0.25] = 0
+    if not seqlens.any():
+        seqlens[-1] = 65
+    pages = int(((seqlens.astype(np.int64) + 63) // 64).sum())
+    for parts in sorted({1, 7, 256, min(max(1, pages // 2), 65536), min(pages + 5, 65536)}):
+        meta = mla.get_split_metadata(torch.from_numpy(seqlens).cuda(), 16, 1, parts)
+        host = mla.split_metadata_host(seqlens, 16, 1, parts)
+        dev = meta.metadata.cpu().numpy()
+        used = 16 + 8 * int(host[2]) + 4 * int(host[1]) + int(host[8]) * int(host[1])
+        assert np.array_equal(dev[:used], host[:used]), f"device metadata differs, batch={batch} parts={parts}"
+
+
 def test_run_to_run_bitwise():
     inp = make_inputs([3000, 77, 4097], 2, 128, seed=28, causal=True)
     a = run_decode(inp)
